@@ -1,0 +1,173 @@
+/*
+ * iskv.h -- C ABI of the MI355X (gfx950) iS-KV compressed KV cache.
+ *
+ * Method: page "iS-KV: Online Low-Rank KV Cache Compression via
+ * Block-Incremental SVD". Each K and each V stream of every
+ * (batch, layer, kv-head) keeps
+ *   - an exact window of the most recent rows at input precision
+ *     (section "Architecture Overview"), and
+ *   - a low-rank history C = U Sigma (n x k), sigma (k) and basis B (d x k),
+ *     k <= r, updated block by block: the oldest b window rows F are folded
+ *     in with one core SVD of Z = [Sigma 0; FB FP], and both the basis and
+ *     every stored row's coordinates are rotated and truncated
+ *     (section "Block-Incremental Decoding Updates"; equations for Z,
+ *     SVD_r(Z), U+ and B+).
+ * Decode attention runs on the factors: a history row's score is
+ * (C B_K^T) q = C (B_K^T q), and the weighted history values are
+ * (p^T C_V) B_V^T, which equals dense attention over the reconstruction of
+ * section "Reconstruction and Storage".
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers (HIP device memory) unless the
+ *     argument says "host". Layouts are row-major and dense.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. All device work is enqueued on it, in call order; pointers
+ *     must stay valid until that work has completed. No entry point
+ *     synchronizes except iskv_status.
+ *   - The library never allocates device memory: the caller owns the
+ *     workspace (sized by iskv_workspace_bytes) and every input/output.
+ *     The handle owns host metadata only and is released by iskv_destroy.
+ *   - Return value: ISKV_OK (0) or a negative iskv_status. Argument,
+ *     capacity and workspace errors are detected on the host before anything
+ *     is enqueued and leave the state unchanged. A failed kernel launch
+ *     poisons the handle (ISKV_ERR_POISONED from then on). Numeric trouble
+ *     inside kernels (core SVD iteration cap, non-finite values) sets sticky
+ *     device flags read by iskv_status.
+ *   - Counters n (history rows), e (window rows) and k (rank) are kept per
+ *     layer; all sequences of a batch advance in lockstep.
+ *   - Calls that overlap on the same handle from several host threads race;
+ *     serialize them.
+ */
+#ifndef ISKV_H_
+#define ISKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISKV_API __attribute__((visibility("default")))
+
+typedef enum {
+  ISKV_OK = 0,
+  ISKV_ERR_ARG = -1,       /* invalid argument or configuration */
+  ISKV_ERR_WORKSPACE = -2, /* workspace too small or misaligned */
+  ISKV_ERR_CAPACITY = -3,  /* max_tokens would be exceeded */
+  ISKV_ERR_HIP = -4,       /* a HIP runtime call failed */
+  ISKV_ERR_NUMERIC = -5,   /* returned by iskv_status when a numeric flag is set */
+  ISKV_ERR_POISONED = -6,  /* an earlier launch failed; the handle is unusable */
+  ISKV_ERR_STATE = -7      /* call not valid in the current state (e.g. empty cache) */
+} iskv_status_code;
+
+typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1 } iskv_dtype;
+
+/* Numeric status flags (bit mask returned by iskv_status). */
+#define ISKV_FLAG_SWEEP_CAP 0x1u /* a core SVD stopped at its sweep cap */
+#define ISKV_FLAG_NONFINITE 0x2u /* a core produced a non-finite singular value */
+
+typedef struct {
+  int32_t batch;       /* sequences, >= 1 */
+  int32_t layers;      /* >= 1 */
+  int32_t kv_heads;    /* >= 1 */
+  int32_t q_heads;     /* multiple of kv_heads; query head h reads kv head h / (q_heads/kv_heads) */
+  int32_t head_dim;    /* d; must be 128 */
+  int32_t block;       /* b, rows per fold; 1 <= b <= 128 */
+  int32_t rank_k;      /* r_K, rank budget of keys; 1 <= r_K <= 128 */
+  int32_t rank_v;      /* r_V, rank budget of values; 1 <= r_V <= 128 */
+  int32_t window;      /* w >= 0: exact rows kept after a fold; w + 2b <= 4096 */
+  int32_t max_tokens;  /* per-sequence capacity: n + e <= max_tokens */
+  int32_t coord_dtype; /* iskv_dtype of C = U Sigma; B and sigma are always fp32 */
+  int32_t kv_dtype;    /* iskv_dtype of incoming rows, window, queries and outputs */
+} iskv_config;
+
+typedef struct iskv_ctx *iskv_t;
+
+/* Bytes of device workspace needed for `cfg`; 0 if cfg is invalid. */
+ISKV_API size_t iskv_workspace_bytes(const iskv_config *cfg);
+
+/* Validate cfg, carve the caller's device workspace `dev_ws` (>= 256-byte
+ * aligned, ws_bytes >= iskv_workspace_bytes(cfg)) and clear it on `stream`.
+ * On success *out (host) receives a new handle with every layer empty. */
+ISKV_API int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *stream, iskv_t *out);
+
+/* Forget all tokens (host counters only; state memory is overwritten as the
+ * cache refills) and clear the numeric flags on `stream`. */
+ISKV_API int iskv_reset(iskv_t h, void *stream);
+
+/* Append `nrows` (1..b) new K and V rows per sequence and kv head to layers
+ * layer0 .. layer0+nlayers-1. k_rows, v_rows: [batch][nlayers][kv_heads][nrows][d]
+ * in kv_dtype. Rows enter the exact window; when a layer's window then holds
+ * >= w + b rows, its oldest b rows are folded into the history (at most one
+ * fold per call). Section "Block-Incremental Decoding Updates". */
+ISKV_API int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows,
+                      int32_t layer0, int32_t nlayers, void *stream);
+
+/* Prompt compression without a window: fold exactly b rows per sequence and
+ * kv head straight into the history of layers layer0..layer0+nlayers-1.
+ * Requires every such layer's window to be empty (e == 0). Layout as in
+ * iskv_append_block with nrows = b. */
+ISKV_API int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t layer0,
+                       int32_t nlayers, void *stream);
+
+/* Single-token decode attention over history factors plus the exact window
+ * for layers layer0..layer0+nlayers-1: for every query head,
+ *   out = softmax(scale * [C_K (B_K^T q); K_win q]) applied to [C_V B_V^T; V_win].
+ * q: [batch][nlayers][q_heads][d] in kv_dtype; out: same shape in fp32 (the
+ * compute type; rounding it to bf16 would cost up to 2^-8 relative). Every
+ * layer in range must hold at least one token (else ISKV_ERR_STATE). */
+ISKV_API int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers,
+                     float scale, void *stream);
+
+/* Reconstruction of one unit (section "Reconstruction and Storage"):
+ * dev_out [(n+e) x d] fp32 = history rows C B^T, then the window rows
+ * oldest first. which: 0 = K, 1 = V. */
+ISKV_API int iskv_reconstruct(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head,
+                     float *dev_out, void *stream);
+
+/* Host-known counters of a layer (no device access): history rows n, window
+ * rows e, key rank k_k and value rank k_v. Pointers are host pointers. */
+ISKV_API int iskv_counts(iskv_t h, int32_t layer, int32_t *n, int32_t *e, int32_t *k_k, int32_t *k_v);
+
+/* Copy one unit's state out (device to device): C [n x r] in coord_dtype
+ * (columns >= k are zero), sigma [r] fp32, Bt [r x d] fp32 (row j = basis
+ * vector j), window [e x d] in kv_dtype oldest first. Any pointer may be NULL
+ * to skip that part. */
+ISKV_API int iskv_export_state(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head, void *C,
+                      float *sigma, float *Bt, void *window, void *stream);
+
+/* Set a layer's counters (host), e.g. before importing a checkpoint.
+ * Requires n % b == 0, k_k <= min(r_K, n, d), k_v <= min(r_V, n, d),
+ * 0 <= e < w + b, n + e <= max_tokens. */
+ISKV_API int iskv_set_counts(iskv_t h, int32_t layer, int32_t n, int32_t e, int32_t k_k, int32_t k_v);
+
+/* Copy one unit's state in (device to device), layouts as iskv_export_state,
+ * with the layer's current counters; NULL pointers leave that part as is.
+ * The caller is responsible for the state being a valid factorization
+ * (orthonormal Bt rows, zero C columns >= k). */
+ISKV_API int iskv_import_state(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head,
+                      const void *C, const float *sigma, const float *Bt, const void *window,
+                      void *stream);
+
+/* Per-unit statistics of each unit's most recent fold (device to device):
+ * sweeps [units] int32 = core SVD sweeps; discarded [units] fp32 = energy
+ * (sum of squared singular values) dropped by truncation. Units are ordered
+ * [layers][batch][kv_heads]. Either pointer may be NULL. */
+ISKV_API int iskv_fold_stats(iskv_t h, int32_t which, int32_t *sweeps, float *discarded, void *stream);
+
+/* Synchronize `stream` and read the sticky numeric flags (host *flags).
+ * Returns ISKV_ERR_NUMERIC if any flag is set, else ISKV_OK. */
+ISKV_API int iskv_status(iskv_t h, void *stream, uint32_t *flags);
+
+/* Release the handle (host memory only; the workspace stays the caller's). */
+ISKV_API int iskv_destroy(iskv_t h);
+
+/* Static description of a status code. */
+ISKV_API const char *iskv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISKV_H_ */

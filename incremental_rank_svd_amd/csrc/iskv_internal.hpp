@@ -1,0 +1,149 @@
+// Internal declarations of the gfx950 iS-KV library: state layout in HBM,
+// kernel argument blocks, small device helpers and the kernel launchers.
+// Every kernel is hand-written HIP for gfx950 (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace iskv {
+
+constexpr int D = 128;         // head dimension
+constexpr int NT = 256;        // threads per workgroup (4 wavefronts)
+constexpr int SWEEP_CAP = 40;  // core SVD sweep cap (flagged when reached)
+
+constexpr uint32_t FLAG_SWEEP_CAP = 0x1u;
+constexpr uint32_t FLAG_NONFINITE = 0x2u;
+
+// Device buffers of one stream kind (K or V), all carved from the caller's
+// workspace. Units are ordered [layer][batch][kv_head] so a layer range is a
+// contiguous unit range.
+struct Stream {
+  void *C;          // [U][ncap][r] coordinates C = U Sigma (coord dtype), zero beyond column k
+  float *Bt;        // [U][r][D] basis vectors as rows, zero beyond row k
+  float *sig;       // [U][r] singular values, zero beyond k
+  void *ring;       // [U][rcap][D] exact window ring (kv dtype)
+  float *Htop;      // [U][r][r] scratch: signed, sorted H[0:k, 0:k+] of the last fold
+  float *P;         // [U][min(b, D)][D] scratch: residual basis rows of the last fold
+  float *YFP;       // [U][bmax][D] scratch: rows [F B | F P] of the last fold
+  int32_t *sweeps;  // [U] core sweeps of the last fold
+  float *disc;      // [U] energy dropped by the last fold
+  int r;            // rank budget
+};
+
+struct Layout {
+  int batch, layers, kvh, qh, g;  // g = query heads per kv head
+  int b, w, ncap, rcap;           // block, window, history capacity, ring capacity
+  int coord_bf16, kv_bf16;
+  int units;                      // batch * layers * kvh
+  Stream X[2];                    // 0 = K, 1 = V
+  uint32_t *status;               // [16] sticky numeric flags
+  // decode scratch
+  uint32_t *ticket;  // [U] decode blocks finished per unit (reset to 0 by the last one)
+  float *part;    // [U][nchunk_max][g][2 + rV] per-chunk (max, sum, o')
+  float *wpart;   // [U][g][2 + D] window part (max, sum, o)
+  int chunk;      // history rows per decode chunk
+  int nchunk_max;
+};
+
+struct FoldArgs {
+  Stream X;
+  int u0;            // first unit of the launch
+  int n, k, b, r;    // history rows, rank before the fold, block, rank budget
+  int rcap, head;    // ring capacity and ring index of F's first row
+  int ncap, bmax;
+  int pmax;          // rows per unit of the residual-basis scratch, min(b, D)
+  uint32_t *status;
+  int lds_small;     // float offset of the small arrays in dynamic LDS
+};
+
+struct RewriteArgs {
+  Stream X;
+  int u0, n, k, kp, r, ncap;
+};
+
+struct IngestArgs {
+  const void *src[2];  // K, V rows [batch][nl_in][kvh][nrows][D]
+  void *ring[2];
+  int batch, kvh, nl_in, lrel0, nl;  // input layer count, first input layer of the run, layers in run
+  int u0, nrows, rcap, pos;          // ring index of the first new row
+};
+
+struct DecodeArgs {
+  Layout L;
+  const void *q;  // [batch][nl_in][qh][D] in kv dtype
+  void *out;      // [batch][nl_in][qh][D] fp32
+  int nl_in, lrel0, nl, u0;
+  int n, e, kK, kV, head;
+  int nchunk;
+  float scale;
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float ldf<float>(const float *p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ldf<uint16_t>(const uint16_t *p, size_t i) { return bf2f(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void stf(T *p, size_t i, float v);
+template <>
+__device__ __forceinline__ void stf<float>(float *p, size_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void stf<uint16_t>(uint16_t *p, size_t i, float v) { p[i] = f2bf(v); }
+
+// sum over the 16 lanes of an aligned lane group
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  return v;
+}
+
+__device__ __forceinline__ float sum64(float v) {
+  v += __shfl_xor(v, 32);
+  v += __shfl_xor(v, 16);
+  return sum16(v);
+}
+
+__device__ __forceinline__ float max64(float v) {
+  v = fmaxf(v, __shfl_xor(v, 32));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 1));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns the hipError_t of its launch)
+// ---------------------------------------------------------------------------
+size_t core_lds_bytes(int k, int b, int r);
+hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
+hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);
+hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, int e, int head,
+                              float *out, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_ring_copy(const Layout &L, int which, int u, int e, int head, void *dst,
+                            const void *src, int to_ring, hipStream_t s);
+
+}  // namespace iskv

@@ -1,0 +1,131 @@
+// Small kernels: window ingest, reconstruction, zero fill, ring copies.
+#include "iskv_internal.hpp"
+
+namespace iskv {
+
+namespace {
+
+// Copy nrows new rows per unit into the window ring (section "Architecture
+// Overview": the most recent rows are kept exactly). blockIdx.y selects K/V.
+// One thread moves 4 bytes.
+__global__ void __launch_bounds__(NT) k_ingest(const IngestArgs a, int elem_bytes) {
+  const int which = blockIdx.y;
+  const int words_per_row = D * elem_bytes / 4;
+  const size_t total = (size_t)a.batch * a.nl * a.kvh * a.nrows * words_per_row;
+  const uint32_t *src = (const uint32_t *)a.src[which];
+  uint32_t *ring = (uint32_t *)a.ring[which];
+  for (size_t idx = (size_t)blockIdx.x * NT + threadIdx.x; idx < total; idx += (size_t)gridDim.x * NT) {
+    const int wd = (int)(idx % words_per_row);
+    size_t t = idx / words_per_row;
+    const int i = (int)(t % a.nrows);
+    t /= a.nrows;
+    const int h = (int)(t % a.kvh);
+    t /= a.kvh;
+    const int li = (int)(t % a.nl);
+    const int bi = (int)(t / a.nl);
+    const size_t s_off =
+        ((((size_t)bi * a.nl_in + a.lrel0 + li) * a.kvh + h) * a.nrows + i) * words_per_row + wd;
+    const size_t u = (size_t)a.u0 + ((size_t)li * a.batch + bi) * a.kvh + h;
+    int pos = a.pos + i;
+    if (pos >= a.rcap) pos -= a.rcap;
+    ring[(u * a.rcap + pos) * words_per_row + wd] = src[s_off];
+  }
+}
+
+// X~ = [C B^T ; window] for one unit (section "Reconstruction and Storage").
+template <typename TC, typename TK>
+__global__ void __launch_bounds__(NT) k_reconstruct(const float *Bt, const TC *C, const TK *ring,
+                                                    int r, int n, int k, int e, int head, int rcap,
+                                                    float *out) {
+  const int row = blockIdx.x;
+  if (row < n) {
+    for (int t = threadIdx.x; t < D; t += NT) {
+      float s = 0.f;
+      for (int j = 0; j < k; j++) s += ldf<TC>(C, (size_t)row * r + j) * Bt[(size_t)j * D + t];
+      out[(size_t)row * D + t] = s;
+    }
+  } else {
+    int pos = head + (row - n);
+    if (pos >= rcap) pos -= rcap;
+    for (int t = threadIdx.x; t < D; t += NT) out[(size_t)row * D + t] = ldf<TK>(ring, (size_t)pos * D + t);
+  }
+}
+
+__global__ void k_zero(uint32_t *p, size_t nwords) {
+  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < nwords; i += (size_t)gridDim.x * NT) p[i] = 0u;
+}
+
+// Window rows between the ring (starting at head, wrapping) and a dense buffer.
+__global__ void k_ring_copy(uint8_t *ring, uint8_t *dense, int e, int head, int rcap, int row_bytes,
+                            int to_ring) {
+  const int i = blockIdx.x;
+  int pos = head + i;
+  if (pos >= rcap) pos -= rcap;
+  for (int t = threadIdx.x; t < row_bytes; t += NT) {
+    if (to_ring)
+      ring[(size_t)pos * row_bytes + t] = dense[(size_t)i * row_bytes + t];
+    else
+      dense[(size_t)i * row_bytes + t] = ring[(size_t)pos * row_bytes + t];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s) {
+  const int eb = kv_bf16 ? 2 : 4;
+  const size_t total = (size_t)a.batch * a.nl * a.kvh * a.nrows * (D * eb / 4);
+  size_t blocks = (total + NT - 1) / NT;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_ingest, dim3((unsigned)blocks, 2), dim3(NT), 0, s, a, eb);
+  return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, int e, int head,
+                              float *out, hipStream_t s) {
+  const Stream &X = L.X[which];
+  const int rows = n + e;
+  if (rows == 0) return hipSuccess;
+  const float *Bt = X.Bt + (size_t)u * X.r * D;
+  const size_t coff = (size_t)u * L.ncap * X.r;
+  const size_t roff = (size_t)u * L.rcap * D;
+  if (L.coord_bf16 && L.kv_bf16)
+    hipLaunchKernelGGL((k_reconstruct<uint16_t, uint16_t>), dim3(rows), dim3(NT), 0, s, Bt,
+                       (const uint16_t *)X.C + coff, (const uint16_t *)X.ring + roff, X.r, n, k, e, head,
+                       L.rcap, out);
+  else if (L.coord_bf16)
+    hipLaunchKernelGGL((k_reconstruct<uint16_t, float>), dim3(rows), dim3(NT), 0, s, Bt,
+                       (const uint16_t *)X.C + coff, (const float *)X.ring + roff, X.r, n, k, e, head,
+                       L.rcap, out);
+  else if (L.kv_bf16)
+    hipLaunchKernelGGL((k_reconstruct<float, uint16_t>), dim3(rows), dim3(NT), 0, s, Bt,
+                       (const float *)X.C + coff, (const uint16_t *)X.ring + roff, X.r, n, k, e, head,
+                       L.rcap, out);
+  else
+    hipLaunchKernelGGL((k_reconstruct<float, float>), dim3(rows), dim3(NT), 0, s, Bt,
+                       (const float *)X.C + coff, (const float *)X.ring + roff, X.r, n, k, e, head,
+                       L.rcap, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + NT - 1) / NT;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(NT), 0, s, (uint32_t *)p, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_copy(const Layout &L, int which, int u, int e, int head, void *dst,
+                            const void *src, int to_ring, hipStream_t s) {
+  if (e <= 0) return hipSuccess;
+  const int row_bytes = D * (L.kv_bf16 ? 2 : 4);
+  uint8_t *ring = (uint8_t *)L.X[which].ring + (size_t)u * L.rcap * row_bytes;
+  uint8_t *dense = (uint8_t *)(to_ring ? src : dst);
+  hipLaunchKernelGGL(k_ring_copy, dim3(e), dim3(NT), 0, s, ring, dense, e, head, L.rcap, row_bytes,
+                     to_ring);
+  return hipGetLastError();
+}
+
+}  // namespace iskv
