@@ -64,7 +64,7 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
   l.kv_bf16 = c->kv_dtype == ISKV_BF16;
   l.units = c->batch * c->layers * c->kv_heads;
   l.chunk = 512 > l.rcap ? 512 : l.rcap;
-  l.nchunk_max = (l.ncap + l.chunk - 1) / l.chunk;
+  l.nchunk_max = (l.ncap + 511) / 512;  // every decode path uses >= 512 history rows per block
   if (l.nchunk_max < 1) l.nchunk_max = 1;
   const size_t U = (size_t)l.units;
   const size_t cb = l.coord_bf16 ? 2 : 4, kb = l.kv_bf16 ? 2 : 4;
@@ -323,7 +323,8 @@ int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_
     a.kK = h->kk[l0];
     a.kV = h->kv[l0];
     a.head = h->head[l0];
-    a.nchunk = (a.n + h->L.chunk - 1) / h->L.chunk;
+    const int chunk = decode_chunk_rows(h->L);
+    a.nchunk = (a.n + chunk - 1) / chunk;
     a.scale = scale;
     int rc = fail_hip(h, launch_decode(a, s));
     if (rc) return rc;

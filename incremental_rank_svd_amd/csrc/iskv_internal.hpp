@@ -140,6 +140,7 @@ hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf1
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+int decode_chunk_rows(const Layout &L);  // history rows per decode block
 hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, int e, int head,
                               float *out, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);

@@ -267,6 +267,371 @@ __global__ void __launch_bounds__(NT) k_decode(const DecodeArgs a) {
   if (tid == 0) a.L.ticket[u] = 0u;
 }
 
+
+// ===========================================================================
+// bf16 storage: matrix-core decode (used when both ranks are multiples of 8)
+//
+// Each history wavefront takes a contiguous range of rows, in steps of 32
+// rows, with v_mfma_f32_16x16x32_bf16:
+//   scores   S (16 rows x 16 heads) = C_K tile (16 x 32 cols) . Q' (32 x 16)
+//            A: 16 contiguous bytes of one C_K row per lane (coalesced);
+//            B: q' in registers, split into bf16 hi + lo (about 16 bits).
+//   values   o'^T (16 cols x 16 heads) += C_V^T (16 x 32 rows) . P^T (32 x 16)
+//            The 32 K-slots of the step are ordered so that lane l's eight
+//            softmax weights are exactly the eight scores its own output
+//            fragments hold (rows 4q..4q+3 and 16+4q..16+4q+3, q = l/16);
+//            P^T is then split hi + lo in registers, and the C_V^T fragment is
+//            gathered from a per-wave LDS copy of the 32-row tile.
+// Online softmax per wave (running max and sum per head); the waves of the
+// unit's workgroup are then combined in LDS.
+// ===========================================================================
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// x = hi + lo with both parts bf16 (round to nearest even)
+__device__ __forceinline__ void split8(const float *x, u32x4_t &hi, u32x4_t &lo) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    h[i] = f2bf(x[i]);
+    l[i] = f2bf(x[i] - bf2f(h[i]));
+  }
+  hi = u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+  lo = u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+}
+
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__host__ __device__ __forceinline__ int tile_stride(int rsV) { return ((rsV + 15) / 16) * 16 + 4; }
+
+// One 1024-thread workgroup per unit: wavefronts 0..nhw-1 stream the history
+// rows (MFMA scores and values, online softmax), the last wavefront does the
+// window rows when there are any; the waves are combined in LDS and the
+// workgroup writes the unit's outputs. No workgroup talks to another, so no
+// device-scope fence is needed (on a multi-XCD part each one writes back and
+// invalidates the XCD's L2).
+constexpr int NTU = 1024;
+constexpr int NWU = NTU / 64;
+constexpr int WH = 2;  // window heads per pass (register budget: 128 VGPRs per lane)
+
+__host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV) {
+  const size_t qs = (size_t)MAXG * (rsK > 0 ? rsK : 1) + 4 * 64 * 2 * 4;  // q' + fragments
+  const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;  // floats
+  const size_t comb = (size_t)NWU * MAXG * (2 + rsV) + (size_t)MAXG * (2 + D) + (size_t)MAXG * rsV + 8 * MAXG;
+  return sizeof(float) * (qs + (tiles > comb ? tiles : comb));
+}
+
+template <int KS, int NTV>
+__global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
+  extern __shared__ float sm[];
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int g = a.L.g, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rsK = a.L.X[0].r, rsV = a.L.X[1].r;
+  float *qsm = sm;                                  // g x rsK: q'
+  float *big = sm + (size_t)MAXG * rsK + 4 * 64 * 2 * 4;  // after q' and its fragments
+  int li, bi, h;
+  unit_coords(a, ul, li, bi, h);
+  const uint16_t *q = (const uint16_t *)a.q + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
+  // q' = scale * B_K^T q, zero beyond the current rank (16 lanes per dot)
+  {
+    const float *Bt = a.L.X[0].Bt + (size_t)u * rsK * D;
+    const int l16 = tid & 15, grp = tid >> 4;
+    for (int pj = grp; pj < g * rsK; pj += NTU / 16) {
+      const int hh = pj / rsK, jj = pj - hh * rsK;
+      float s = 0.f;
+      if (jj < a.kK) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) s += Bt[(size_t)jj * D + l16 * 8 + t] * bf2f(q[(size_t)hh * D + l16 * 8 + t]);
+      }
+      s = sum16(s);
+      if (l16 == 0) qsm[hh * rsK + jj] = a.scale * s;
+    }
+  }
+  __syncthreads();
+  // MFMA B fragments of q' (bf16 hi and lo) per lane, shared by all waves:
+  // frag[(kc * 2 + part) * 64 + lane]
+  u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);
+  if (tid < 64 * KS) {
+    const int kc = tid >> 6, ln = tid & 63;
+    const int fq = ln & 15, fd = ln >> 4;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int col = kc * 32 + 8 * fd + i;
+      x[i] = (fq < g && col < rsK) ? qsm[fq * rsK + col] : 0.f;
+    }
+    split8(x, frag[(kc * 2) * 64 + ln], frag[(kc * 2 + 1) * 64 + ln]);
+  }
+  __syncthreads();
+  const bool has_win = a.e > 0;
+  const int nhw = has_win ? NWU - 1 : NWU;  // history waves
+  const int hq = lane & 15, qd = lane >> 4;
+  // per-wave results kept in registers until the loops are done
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[NTV];
+#pragma unroll
+  for (int nt = 0; nt < NTV; nt++) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // window wave results (heads in groups of 4, kept per group in LDS later)
+  if (wv < nhw) {
+    int per = (a.n + nhw - 1) / nhw;
+    per = ((per + 31) / 32) * 32;
+    const int wb = wv * per;
+    const int we = min(a.n, wb + per);
+    const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.ncap * rsK;
+    const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.ncap * rsV;
+    const int ts = tile_stride(rsV);
+    uint16_t *tile = (uint16_t *)big + (size_t)wv * 32 * ts;
+    const int cpr = rsV / 8;
+    for (int rb = wb; rb < we; rb += 32) {
+      // C_K fragments of rows rb..rb+15 and rb+16..rb+31 (issued first)
+      u32x4_t ka[KS], kb[KS];
+#pragma unroll
+      for (int kc = 0; kc < KS; kc++) {
+        const int col = kc * 32 + 8 * qd;
+        const int r0 = rb + hq, r1 = rb + 16 + hq;
+        ka[kc] = u32x4_t{0u, 0u, 0u, 0u};
+        kb[kc] = u32x4_t{0u, 0u, 0u, 0u};
+        if (col < rsK) {
+          if (r0 < we) ka[kc] = *(const u32x4_t *)(CK + (size_t)r0 * rsK + col);
+          if (r1 < we) kb[kc] = *(const u32x4_t *)(CK + (size_t)r1 * rsK + col);
+        }
+      }
+      // the 32-row C_V tile (32 x rsV/8 chunks of 16 bytes; 64 * NTV >= 4 * rsV)
+      // goes straight to this wave's LDS tile once it has arrived
+#pragma unroll
+      for (int z = 0; z < NTV; z++) {
+        const int idx = lane + 64 * z;
+        const int rr = idx / cpr, c8 = idx - rr * cpr;
+        if (idx < 32 * cpr) {
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          if (rb + rr < we) v = *(const u32x4_t *)(CV + (size_t)(rb + rr) * rsV + c8 * 8);
+          uint2 *dstp = (uint2 *)(tile + rr * ts + c8 * 8);
+          dstp[0] = uint2{v[0], v[1]};
+          dstp[1] = uint2{v[2], v[3]};
+        }
+      }
+      f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KS; kc++) {
+        const u32x4_t bh = frag[(kc * 2) * 64 + lane], bl = frag[(kc * 2 + 1) * 64 + lane];
+        d0 = mfma16(ka[kc], bh, d0);
+        d0 = mfma16(ka[kc], bl, d0);
+        d1 = mfma16(kb[kc], bh, d1);
+        d1 = mfma16(kb[kc], bl, d1);
+      }
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s[i] = (rb + 4 * qd + i < we) ? d0[i] : -INFINITY;
+        s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 8; i++) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      const float al = __expf(m - ms);
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        p[i] = __expf(s[i] - ms);
+        ps += p[i];
+      }
+      l = l * al + ps;
+      m = mn;
+#pragma unroll
+      for (int nt = 0; nt < NTV; nt++) acc[nt] *= al;
+      u32x4_t phi, plo;
+      split8(p, phi, plo);
+      wave_fence();
+#pragma unroll
+      for (int nt = 0; nt < NTV; nt++) {
+        const int col = nt * 16 + hq;
+        uint16_t v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int row = (i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4);
+          v8[i] = (col < rsV) ? tile[row * ts + col] : (uint16_t)0;
+        }
+        const u32x4_t av = {pack2(v8[0], v8[1]), pack2(v8[2], v8[3]), pack2(v8[4], v8[5]), pack2(v8[6], v8[7])};
+        acc[nt] = mfma16(av, phi, acc[nt]);
+        acc[nt] = mfma16(av, plo, acc[nt]);
+      }
+      wave_fence();
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+  }
+  __syncthreads();  // tiles are free from here on
+  float *hm = big;                                  // [NWU][MAXG] max
+  float *hl = hm + NWU * MAXG;                      // [NWU][MAXG] sum
+  float *ha = hl + NWU * MAXG;                      // [NWU][MAXG][rsV] o'
+  float *wo = ha + (size_t)NWU * MAXG * rsV;        // [MAXG][2 + D] window (m, l, o)
+  float *op = wo + (size_t)MAXG * (2 + D);          // [MAXG][rsV] merged o'
+  float *fac = op + (size_t)MAXG * rsV;             // [MAXG][8]: M, L, window factor
+  if (wv < nhw) {
+    if (hq < g) {
+      if (qd == 0) {
+        hm[wv * MAXG + hq] = m;
+        hl[wv * MAXG + hq] = l;
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTV; nt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int col = nt * 16 + 4 * qd + i;
+          if (col < rsV) ha[((size_t)wv * MAXG + hq) * rsV + col] = acc[nt][i];
+        }
+    }
+  } else {
+    // window rows: 4 lane groups of 16, 16 lanes per 128-wide row
+    const int l16 = lane & 15, grp = lane >> 4;
+    const uint16_t *kr = (const uint16_t *)a.L.X[0].ring + (size_t)u * a.L.rcap * D;
+    const uint16_t *vr = (const uint16_t *)a.L.X[1].ring + (size_t)u * a.L.rcap * D;
+    for (int h0 = 0; h0 < g; h0 += WH) {
+      float qv[WH][8], wa[WH][8], wm[WH], wl[WH];
+#pragma unroll
+      for (int j = 0; j < WH; j++) {
+        wm[j] = -INFINITY;
+        wl[j] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          wa[j][t] = 0.f;
+          qv[j][t] = (h0 + j < g) ? a.scale * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
+        }
+      }
+      for (int i = grp; i < a.e; i += 4) {
+        int pos = a.head + i;
+        if (pos >= a.L.rcap) pos -= a.L.rcap;
+        const u32x4_t kw = *(const u32x4_t *)(kr + (size_t)pos * D + l16 * 8);
+        const u32x4_t vw = *(const u32x4_t *)(vr + (size_t)pos * D + l16 * 8);
+        float kx[8], vx[8];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          kx[2 * t] = __uint_as_float(kw[t] << 16);
+          kx[2 * t + 1] = __uint_as_float(kw[t] & 0xffff0000u);
+          vx[2 * t] = __uint_as_float(vw[t] << 16);
+          vx[2 * t + 1] = __uint_as_float(vw[t] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < WH; j++) {
+          float sc = 0.f;
+#pragma unroll
+          for (int t = 0; t < 8; t++) sc += kx[t] * qv[j][t];
+          sc = sum16(sc);
+          const float mn = fmaxf(wm[j], sc);
+          const float al = __expf(wm[j] - mn);
+          const float pv = __expf(sc - mn);
+          wl[j] = wl[j] * al + pv;
+#pragma unroll
+          for (int t = 0; t < 8; t++) wa[j][t] = wa[j][t] * al + pv * vx[t];
+          wm[j] = mn;
+        }
+      }
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < WH; j++) {
+          const float mo = __shfl_xor(wm[j], off);
+          const float lo = __shfl_xor(wl[j], off);
+          const float mn = fmaxf(wm[j], mo);
+          const float ms = (mn == -INFINITY) ? 0.f : mn;
+          const float f0 = __expf(wm[j] - ms), f1 = __expf(mo - ms);
+          wl[j] = wl[j] * f0 + lo * f1;
+#pragma unroll
+          for (int t = 0; t < 8; t++) {
+            const float ao = __shfl_xor(wa[j][t], off);
+            wa[j][t] = wa[j][t] * f0 + ao * f1;
+          }
+          wm[j] = mn;
+        }
+      }
+      if (grp == 0) {
+#pragma unroll
+        for (int j = 0; j < WH; j++) {
+          if (h0 + j < g) {
+            float *w = wo + (size_t)(h0 + j) * (2 + D);
+            if (l16 == 0) {
+              w[0] = wm[j];
+              w[1] = wl[j];
+            }
+#pragma unroll
+            for (int t = 0; t < 8; t++) w[2 + l16 * 8 + t] = wa[j][t];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // combine: per head the global max M, the sum L and the window factor
+  if (tid < g) {
+    float M = has_win ? wo[tid * (2 + D)] : -INFINITY;
+    for (int w = 0; w < nhw; w++) M = fmaxf(M, hm[w * MAXG + tid]);
+    const float ms = (M == -INFINITY) ? 0.f : M;
+    float L = has_win ? __expf(wo[tid * (2 + D)] - ms) * wo[tid * (2 + D) + 1] : 0.f;
+    for (int w = 0; w < nhw; w++) L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+    fac[tid * 8 + 0] = ms;
+    fac[tid * 8 + 1] = L;
+    fac[tid * 8 + 2] = has_win ? __expf(wo[tid * (2 + D)] - ms) : 0.f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < g * rsV; idx += NTU) {
+    const int hh = idx / rsV, j = idx - hh * rsV;
+    const float ms = fac[hh * 8];
+    float s = 0.f;
+    for (int w = 0; w < nhw; w++) s += __expf(hm[w * MAXG + hh] - ms) * ha[((size_t)w * MAXG + hh) * rsV + j];
+    op[idx] = s;
+  }
+  __syncthreads();
+  const float *Bv = a.L.X[1].Bt + (size_t)u * rsV * D;
+  float *out = (float *)a.out + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
+  for (int idx = tid; idx < g * D; idx += NTU) {
+    const int hh = idx / D, t = idx - hh * D;
+    float s = 0.f;
+    for (int j = 0; j < a.kV; j++) s += op[hh * rsV + j] * Bv[(size_t)j * D + t];
+    if (has_win) s += fac[hh * 8 + 2] * wo[(size_t)hh * (2 + D) + 2 + t];
+    out[idx] = s / fac[hh * 8 + 1];
+  }
+}
+
+template <int KS, int NTV>
+hipError_t launch_bf16_t(const DecodeArgs &a, int nunits, hipStream_t s) {
+  const size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r);
+  hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_unit<KS, NTV>), dim3(nunits), dim3(NTU), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_bf16_ks(const DecodeArgs &a, int nunits, hipStream_t s) {
+  switch ((a.L.X[1].r + 15) / 16) {
+    case 1: return launch_bf16_t<KS, 1>(a, nunits, s);
+    case 2: return launch_bf16_t<KS, 2>(a, nunits, s);
+    case 3: return launch_bf16_t<KS, 3>(a, nunits, s);
+    case 4: return launch_bf16_t<KS, 4>(a, nunits, s);
+    case 5: return launch_bf16_t<KS, 5>(a, nunits, s);
+    case 6: return launch_bf16_t<KS, 6>(a, nunits, s);
+    case 7: return launch_bf16_t<KS, 7>(a, nunits, s);
+    default: return launch_bf16_t<KS, 8>(a, nunits, s);
+  }
+}
+
 template <typename TC, typename TK>
 hipError_t launch_decode_t(const DecodeArgs &a, int nunits, hipStream_t s) {
   const size_t lds = sizeof(float) * (4 * MAXG + QS_FLOATS + (size_t)MAXG * a.L.chunk);
@@ -279,8 +644,18 @@ hipError_t launch_decode_t(const DecodeArgs &a, int nunits, hipStream_t s) {
 
 }  // namespace
 
+int decode_chunk_rows(const Layout &L) { return L.chunk; }
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   const int nunits = a.L.batch * a.nl * a.L.kvh;
+  if (a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0) {
+    switch ((a.L.X[0].r + 31) / 32) {
+      case 1: return launch_bf16_ks<1>(a, nunits, s);
+      case 2: return launch_bf16_ks<2>(a, nunits, s);
+      case 3: return launch_bf16_ks<3>(a, nunits, s);
+      default: return launch_bf16_ks<4>(a, nunits, s);
+    }
+  }
   if (a.L.coord_bf16 && a.L.kv_bf16) return launch_decode_t<uint16_t, uint16_t>(a, nunits, s);
   if (a.L.coord_bf16) return launch_decode_t<uint16_t, float>(a, nunits, s);
   if (a.L.kv_bf16) return launch_decode_t<float, uint16_t>(a, nunits, s);

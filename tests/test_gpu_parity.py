@@ -333,3 +333,25 @@ def test_error_paths_leave_state_unchanged(iskv):
         cache.append_block(K[:, :1, :, :1].contiguous(), K[:, :1, :, :1].contiguous(), layer0=2)
     assert cache.counts(0) == before
     assert cache.status() == 0
+
+
+@pytest.mark.parametrize("rk,rv,g,b", [(64, 96, 1, 128), (128, 8, 8, 64), (8, 128, 2, 64), (48, 24, 4, 64)])
+def test_bf16_decode_rank_and_group_shapes(iskv, rk, rv, g, b):
+    """Matrix-core decode over several rank / GQA-group shapes, history long
+    enough for several 1024-row blocks plus a ragged tail."""
+    from dataclasses import replace
+
+    w = replace(synth.get_config(1), layers=1, kv_heads=2, q_heads=2 * g, block=b, rank_k=rk,
+                rank_v=rv, window=3 * b // 2, decode_tokens=2600, cfg_id=30 + rk + rv + g)
+    note("case: bf16 decode rk=%d rv=%d g=%d b=%d" % (rk, rv, g, b))
+    rows = _rows_all(w, w.total_tokens)
+    cache = _cache(iskv, w)
+    _feed(cache, w, rows, 0, w.total_tokens, b)
+    n, e, kk, kv = cache.counts(0)
+    assert n > 2048 and e > 0
+    for step in range(3):
+        q = _queries(w, step)
+        out = cache.decode_attn(to_dev(q, torch.bfloat16, DEV))
+        derr = _check_decode(cache, w, q, out, [(0, 0, 0), (0, 0, 1)])
+    assert cache.status() == 0
+    note("  decode err %.2e" % derr)
