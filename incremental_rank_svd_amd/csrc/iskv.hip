@@ -136,39 +136,36 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
   const int u0 = l0 * per_layer, nunits = (l1 - l0) * per_layer;
   const int n = h->n[l0];
   int kp[2];
+  FoldArgs a = {};
+  RewriteArgs ra = {};
   for (int x = 0; x < 2; x++) {
     const int k = x == 0 ? h->kk[l0] : h->kv[l0];
-    FoldArgs a = {};
-    a.X = L.X[x];
-    a.u0 = u0;
-    a.n = n;
-    a.k = k;
-    a.b = L.b;
-    a.r = L.X[x].r;
-    a.rcap = L.rcap;
-    a.head = h->head[l0];
-    a.ncap = L.ncap;
-    a.bmax = L.b;
-    a.pmax = L.b < D ? L.b : D;
-    a.status = L.status;
-    int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
-    if (rc) return rc;
     kp[x] = kplus_of(k, L.b, L.X[x].r);
+    a.X[x] = L.X[x];
+    a.k[x] = k;
+    a.r[x] = L.X[x].r;
+    ra.X[x] = L.X[x];
+    ra.k[x] = k;
+    ra.kp[x] = kp[x];
+    ra.r[x] = L.X[x].r;
   }
-  for (int x = 0; x < 2; x++) {
-    const int k = x == 0 ? h->kk[l0] : h->kv[l0];
-    if (n > 0 && k > 0) {
-      RewriteArgs ra = {};
-      ra.X = L.X[x];
-      ra.u0 = u0;
-      ra.n = n;
-      ra.k = k;
-      ra.kp = kp[x];
-      ra.r = L.X[x].r;
-      ra.ncap = L.ncap;
-      int rc = fail_hip(h, launch_rewrite(ra, nunits, L.coord_bf16, s));
-      if (rc) return rc;
-    }
+  a.u0 = u0;
+  a.n = n;
+  a.b = L.b;
+  a.rcap = L.rcap;
+  a.head = h->head[l0];
+  a.ncap = L.ncap;
+  a.bmax = L.b;
+  a.pmax = L.b < D ? L.b : D;
+  a.status = L.status;
+  int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
+  if (rc) return rc;
+  if (n > 0) {
+    ra.u0 = u0;
+    ra.n = n;
+    ra.ncap = L.ncap;
+    rc = fail_hip(h, launch_rewrite(ra, nunits, L.coord_bf16, s));
+    if (rc) return rc;
   }
   for (int l = l0; l < l1; l++) {
     h->n[l] += L.b;

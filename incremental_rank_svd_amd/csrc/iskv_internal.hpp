@@ -47,20 +47,23 @@ struct Layout {
   int nchunk_max;
 };
 
+// One fold round: both stream kinds in one launch (blockIdx.y = 0 keys, 1 values).
 struct FoldArgs {
-  Stream X;
+  Stream X[2];
+  int k[2], r[2];    // rank before the fold and rank budget, per kind
   int u0;            // first unit of the launch
-  int n, k, b, r;    // history rows, rank before the fold, block, rank budget
+  int n, b;          // history rows, block
   int rcap, head;    // ring capacity and ring index of F's first row
   int ncap, bmax;
   int pmax;          // rows per unit of the residual-basis scratch, min(b, D)
   uint32_t *status;
-  int lds_small;     // float offset of the small arrays in dynamic LDS
+  int lds_small[2];  // float offset of the small arrays in dynamic LDS, per kind
 };
 
 struct RewriteArgs {
-  Stream X;
-  int u0, n, k, kp, r, ncap;
+  Stream X[2];
+  int k[2], kp[2], r[2];
+  int u0, n, ncap;
 };
 
 struct IngestArgs {
@@ -136,8 +139,8 @@ __device__ __forceinline__ float max64(float v) {
 // launchers (each returns the hipError_t of its launch)
 // ---------------------------------------------------------------------------
 size_t core_lds_bytes(int k, int b, int r);
-hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
-hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);
+hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);  // grid (nunits, 2)
+hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);  // K and V
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 int decode_chunk_rows(const Layout &L);  // history rows per decode block

@@ -14,25 +14,43 @@
 // by sigma, since Z H = G Sigma) is split: this kernel writes the b new rows
 // and H_top = H[0:k, 0:k+]; k_rewrite.hip streams the n old rows.
 //
-// Lane groups of 16 lanes do the vector work: a group owns a column (or a
-// row) of 128 / 16 = 8 contiguous elements per lane and reduces with xor
-// shuffles inside the group.
+// Work mapping: quads (4 consecutive lanes) own one Jacobi pair, one
+// Householder column or one column of P; their sums use two DPP quad
+// permutations. Columns in LDS have a stride of 4 (mod 16) floats so that
+// different columns start in different banks.
 #include "iskv_internal.hpp"
 
 namespace iskv {
 
 namespace {
 
-// LDS float counts of each phase (see the kernel body)
-__host__ __device__ inline int core_phase_floats(int k, int b, int r) {
+constexpr int LDA = D + 4;  // LDS stride of the [B | E^T] columns (4 mod 32)
+__host__ __device__ inline int ldz(int m) { return ((m + 31) / 32) * 32 + 4; }
+
+// rows per quad lane of a Jacobi column (a multiple of 4) and column stride
+__host__ __device__ inline int jac_rl(int c) { return 4 * ((c + 15) / 16); }
+__host__ __device__ inline int jac_stride(int c) { return 4 * jac_rl(c) + 4; }
+
+struct CoreLds {
+  int a, z, j, h, total;  // floats: phase A, Z before its QR, J region, H region, max
+};
+
+__host__ __device__ inline CoreLds core_lds(int k, int b, int r) {
+  CoreLds L;
   const int p = (b < D - k) ? b : D - k;
   const int m = k + b, c = k + p;
-  const int sj = 16 * ((c + 15) / 16);
-  int a = (k + b + p) * D;              // phase A: [B; E] rows + P accumulation
-  int z = (m > c) ? m * c : 0;          // phase B: Z before its QR
-  int j = c * D + c * sj;               // phase C/D: J (or B+, or [FB FP]) + H
-  int mx = a > z ? a : z;
-  return mx > j ? mx : j;
+  const int kp = (r < c) ? r : c;
+  const int sj = jac_stride(c);
+  L.a = (k + b) * LDA;
+  L.z = (m > c) ? ldz(m) * c : 0;
+  int jr = c * sj;
+  if (kp * D > jr) jr = kp * D;  // B+ staging
+  if (b * c > jr) jr = b * c;    // [FB FP] staging
+  L.j = (jr + 3) / 4 * 4;  // H (float4 accesses) starts 16-byte aligned
+  L.h = c * sj;
+  int mx = L.a > L.z ? L.a : L.z;
+  L.total = mx > L.j + L.h ? mx : L.j + L.h;
+  return L;
 }
 
 // (column, row) of entry e of a column-major packed upper triangle
@@ -59,178 +77,223 @@ __device__ __forceinline__ void rr_pair(int rnd, int pr, int c2, int &i, int &j)
   j = a < b ? b : a;
 }
 
+// sum over the 4 lanes of a quad (DPP quad permutations, no LDS traffic)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
 // Householder QR (LAPACK dlarfg convention: H = I - tau v v^T, v[0] = 1,
 // H x = beta e_0) of an nrows x ncols matrix stored column-major in LDS with
 // column stride ld; nref reflectors. On return the upper triangle holds R,
-// the part below the diagonal holds v (without the unit head), tau[j] the
-// scalars. Rows of a column are split over the 16 lanes of a group with a
-// stride of 16. All 256 threads must call it.
-__device__ void house_qr(float *A, int ld, int nrows, int ncols, int nref, float *tau) {
-  const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4;
-  for (int j = 0; j < nref; j++) {
+// the part below the diagonal v (without its unit head) and tau[j] the
+// scalars. Quad qid owns the columns qid, qid + 64, ...; lane q of a quad
+// holds rows q, q+4, q+8, ... (consecutive lanes, consecutive words). The
+// owner of column j+1 builds reflector j+1 as soon as it has applied
+// reflector j (one barrier per reflector). ld should be 4 mod 32 so that the
+// columns of different quads start in different banks.
+template <int RQ>
+__device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols, int nref, float *tau) {
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  auto reflector = [&](int j) {
     float *cj = A + (size_t)j * ld;
-    if (tid < 64) {
-      float s = 0.f;
-      for (int t = j + 1 + tid; t < nrows; t += 64) s += cj[t] * cj[t];
-      s = sum64(s);
-      const float x0 = cj[j];
-      float tj = 0.f, beta = x0, scal = 0.f;
-      if (s > 0.f) {
-        beta = -copysignf(sqrtf(x0 * x0 + s), x0);
-        tj = (beta - x0) / beta;
-        scal = 1.f / (x0 - beta);
-      }
-      for (int t = j + 1 + tid; t < nrows; t += 64) cj[t] *= scal;
-      __builtin_amdgcn_wave_barrier();
-      if (tid == 0) {
-        cj[j] = beta;
-        tau[j] = tj;
-      }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < RQ; e++) {
+      const int row = q + 4 * e;
+      if (row > j && row < nrows) s += cj[row] * cj[row];
     }
-    __syncthreads();
+    s = quad_sum(s);
+    const float x0 = cj[j];
+    float tj = 0.f, beta = x0, scal = 0.f;
+    if (s > 0.f) {
+      beta = -copysignf(sqrtf(x0 * x0 + s), x0);
+      tj = (beta - x0) / beta;
+      scal = 1.f / (x0 - beta);
+    }
+#pragma unroll
+    for (int e = 0; e < RQ; e++) {
+      const int row = q + 4 * e;
+      if (row > j && row < nrows) cj[row] *= scal;
+    }
+    if ((j & 3) == q) cj[j] = beta;
+    if (q == 0) tau[j] = tj;
+  };
+  if (nref > 0 && qid == 0) reflector(0);
+  __syncthreads();
+  for (int j = 0; j < nref; j++) {
     const float tj = tau[j];
     if (tj != 0.f) {
-      for (int col = j + 1 + grp; col < ncols; col += 16) {
+      const float *cj = A + (size_t)j * ld;
+      float v[RQ];
+#pragma unroll
+      for (int e = 0; e < RQ; e++) {
+        const int row = q + 4 * e;
+        v[e] = (row < nrows && row >= j) ? ((row == j) ? 1.f : cj[row]) : 0.f;
+      }
+      int col = qid;
+      while (col <= j) col += NT / 4;
+      for (; col < ncols; col += NT / 4) {
+        // two passes over the column (dot, then update): only v stays in registers
         float *cc = A + (size_t)col * ld;
-        float part = 0.f;
-        for (int t = j + 1 + lane; t < nrows; t += 16) part += cj[t] * cc[t];
-        part = sum16(part);
-        const float w = tj * (cc[j] + part);
-        for (int t = j + 1 + lane; t < nrows; t += 16) cc[t] -= w * cj[t];
-        if (lane == 0) cc[j] -= w;
+        float w = 0.f;
+#pragma unroll
+        for (int e = 0; e < RQ; e++) {
+          const int row = q + 4 * e;
+          if (row < nrows && row >= j) w += v[e] * cc[row];
+        }
+        w = tj * quad_sum(w);
+#pragma unroll
+        for (int e = 0; e < RQ; e++) {
+          const int row = q + 4 * e;
+          if (row < nrows && row >= j) cc[row] -= w * v[e];
+        }
       }
     }
+    if (j + 1 < nref && qid == ((j + 1) & (NT / 4 - 1))) reflector(j + 1);
     __syncthreads();
   }
 }
 
-template <int NR, typename TK, typename TC>
-__global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
-  extern __shared__ float smem[];
+// XK (0 keys, 1 values) is a template constant so that every access to the
+// kernel arguments has a constant offset (a dynamic index would copy them to
+// scratch memory).
+template <int NR, typename TK, typename TC, int XK>
+__device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
   const int tid = threadIdx.x, lane = tid & 15, grp = tid >> 4;
+  const int q = tid & 3, qid = tid >> 2;
   const int u = a.u0 + blockIdx.x;
-  const int b = a.b, k = a.k, r = a.r;
+  const Stream &X = a.X[XK];
+  const int b = a.b, k = a.k[XK], r = a.r[XK];
   const int p = (b < D - k) ? b : D - k;
   const int m = k + b, c = k + p;
   const int kplus = (r < c) ? r : c;
-  const int nj = (c + 15) / 16;  // J/H elements per lane per column
-  const int sj = 16 * nj;        // column stride of J and H
+  const int rl = jac_rl(c);      // J/H rows per quad lane
+  const int sj = jac_stride(c);  // column stride of J and H
+  const CoreLds lay = core_lds(k, b, r);
 
-  float *tau = smem + a.lds_small;
+  float *tau = smem + a.lds_small[XK];
   float *sv = tau + D;
   float *sgn = sv + D;
   int *perm = (int *)(sgn + D);
-  int *misc = perm + D;
 
-  const float *Bt = a.X.Bt + (size_t)u * r * D;
-  float *Pg = a.X.P + (size_t)u * a.pmax * D;
-  float *YFP = a.X.YFP + (size_t)u * a.bmax * D;
-  const TK *ring = (const TK *)a.X.ring + (size_t)u * a.rcap * D;
+  const float *Bt = X.Bt + (size_t)u * r * D;
+  float *Pg = X.P + (size_t)u * a.pmax * D;
+  float *YFP = X.YFP + (size_t)u * a.bmax * D;
+  const TK *ring = (const TK *)X.ring + (size_t)u * a.rcap * D;
 
   // ---------------- phase A: projection, residual, residual basis ---------
-  float *A = smem;  // rows 0..k-1 = basis vectors, rows k..k+b-1 = residual rows
-  for (int idx = tid; idx < k * D; idx += NT) A[idx] = Bt[idx];
+  float *A = smem;  // rows 0..k-1 = basis vectors, rows k..k+b-1 = residual rows (stride LDA)
+  // B into LDS, four float4 loads in flight per thread at a time
+  for (int i0 = tid; i0 < k * (D / 4); i0 += 4 * NT) {
+    float4 bq[4];
+#pragma unroll
+    for (int z = 0; z < 4; z++) {
+      const int idx = i0 + NT * z;
+      if (idx < k * (D / 4)) bq[z] = reinterpret_cast<const float4 *>(Bt)[idx];
+    }
+#pragma unroll
+    for (int z = 0; z < 4; z++) {
+      const int idx = i0 + NT * z;
+      if (idx < k * (D / 4)) {
+        const int row = idx / (D / 4), c4 = idx - row * (D / 4);
+        *reinterpret_cast<float4 *>(A + (size_t)row * LDA + 4 * c4) = bq[z];
+      }
+    }
+  }
   float f[NR][8];
 #pragma unroll
-  for (int q = 0; q < NR; q++) {
-    const int i = grp + 16 * q;
+  for (int qq = 0; qq < NR; qq++) {
+    const int i = grp + 16 * qq;
     if (i < b) {
       int ri = a.head + i;
       if (ri >= a.rcap) ri -= a.rcap;
 #pragma unroll
-      for (int t = 0; t < 8; t++) f[q][t] = ldf<TK>(ring, (size_t)ri * D + lane * 8 + t);
+      for (int t = 0; t < 8; t++) f[qq][t] = ldf<TK>(ring, (size_t)ri * D + lane * 8 + t);
     } else {
 #pragma unroll
-      for (int t = 0; t < 8; t++) f[q][t] = 0.f;
+      for (int t = 0; t < 8; t++) f[qq][t] = 0.f;
     }
   }
   __syncthreads();
-  // Y = F B, E = F - Y B^T; then once more against B (E <- E - (E B) B^T, Y += E B)
+  // Y = F B and E = F - Y B^T; then once more E <- E - (E B) B^T
   for (int pass = 0; pass < 2; pass++) {
     for (int j = 0; j < k; j++) {
       float bj[8];
 #pragma unroll
-      for (int t = 0; t < 8; t++) bj[t] = A[j * D + lane * 8 + t];
+      for (int t = 0; t < 8; t++) bj[t] = A[j * LDA + lane * 8 + t];
 #pragma unroll
-      for (int q = 0; q < NR; q++) {
+      for (int qq = 0; qq < NR; qq++) {
         float s = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; t++) s += f[q][t] * bj[t];
+        for (int t = 0; t < 8; t++) s += f[qq][t] * bj[t];
         s = sum16(s);
 #pragma unroll
-        for (int t = 0; t < 8; t++) f[q][t] -= s * bj[t];
-        const int i = grp + 16 * q;
-        if (lane == 0 && i < b) {
-          if (pass == 0)
-            YFP[i * D + j] = s;
-          else
-            YFP[i * D + j] += s;
-        }
+        for (int t = 0; t < 8; t++) f[qq][t] -= s * bj[t];
+        const int i = grp + 16 * qq;
+        if (pass == 0 && lane == 0 && i < b) YFP[i * D + j] = s;
       }
     }
   }
 #pragma unroll
-  for (int q = 0; q < NR; q++) {
-    const int i = grp + 16 * q;
+  for (int qq = 0; qq < NR; qq++) {
+    const int i = grp + 16 * qq;
     if (i < b) {
 #pragma unroll
-      for (int t = 0; t < 8; t++) A[(k + i) * D + lane * 8 + t] = f[q][t];
+      for (int t = 0; t < 8; t++) A[(k + i) * LDA + lane * 8 + t] = f[qq][t];
     }
   }
   __syncthreads();
 
   if (p > 0) {
     // Householder QR of [B | E^T] (column j = LDS row j), c reflectors.
-    house_qr(A, D, D, k + b, c, tau);
-    // P = Q[:, k:k+p] = H_0 ... H_{c-1} [e_k .. e_{k+p-1}], accumulated backwards.
-    // Column q lives in the registers of one lane group (row t = lane + 16e),
-    // so no LDS traffic or barrier is needed between reflectors. Reflectors
-    // j > k+q leave e_{k+q} unchanged and are skipped.
-    float *X = A + (size_t)(k + b) * D;
-    for (int q = grp; q < p; q += 16) {
-      float x[8];
+    house_qr<D / 4>(A, LDA, D, k + b, c, tau);
+    // P = Q[:, k:k+p] = H_0 ... H_{c-1} [e_k .. e_{k+p-1}], accumulated backwards
+    // in the registers of one quad per column (lane q: rows q, q+4, ...);
+    // reflectors j > k+col leave e_{k+col} unchanged and are skipped.
+    for (int col = qid; col < p; col += NT / 4) {
+      float x[D / 4];
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = (lane + 16 * e == k + q) ? 1.f : 0.f;
-      for (int j = k + q; j >= 0; j--) {
+      for (int e = 0; e < D / 4; e++) x[e] = (q + 4 * e == k + col) ? 1.f : 0.f;
+      for (int j = k + col; j >= 0; j--) {
         const float tj = tau[j];
         if (tj == 0.f) continue;
-        const float *cj = A + (size_t)j * D;
-        float part = 0.f;
+        const float *cj = A + (size_t)j * LDA;
+        float w = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int t = lane + 16 * e;
-          part += (t > j) ? cj[t] * x[e] : ((t == j) ? x[e] : 0.f);
+        for (int e = 0; e < D / 4; e++) {
+          const int row = q + 4 * e;
+          w += (row > j) ? cj[row] * x[e] : ((row == j) ? x[e] : 0.f);
         }
-        const float w = tj * sum16(part);
+        w = tj * quad_sum(w);
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int t = lane + 16 * e;
-          x[e] -= (t > j) ? w * cj[t] : ((t == j) ? w : 0.f);
+        for (int e = 0; e < D / 4; e++) {
+          const int row = q + 4 * e;
+          x[e] -= (row > j) ? w * cj[row] : ((row == j) ? w : 0.f);
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; e++) X[(size_t)q * D + lane + 16 * e] = x[e];
+      for (int e = 0; e < D / 4; e++) Pg[(size_t)col * D + q + 4 * e] = x[e];
     }
-    __syncthreads();
-    for (int idx = tid; idx < p * D; idx += NT) Pg[idx] = X[idx];
     // F P = R[k:k+p, k:k+b]^T (lower trapezoidal)
     for (int idx = tid; idx < b * p; idx += NT) {
-      const int i = idx / p, q = idx - i * p;
-      YFP[i * D + k + q] = (q <= i) ? A[(size_t)(k + i) * D + k + q] : 0.f;
+      const int i = idx / p, qq = idx - i * p;
+      YFP[i * D + k + qq] = (qq <= i) ? A[(size_t)(k + i) * LDA + k + qq] : 0.f;
     }
   }
   __syncthreads();
 
   // ---------------- phase B: the matrix J that Jacobi orthogonalizes -------
   // J = Z when Z is square (p == b); otherwise J = R_Z from a QR of Z.
-  float *J = smem;                      // c columns, stride sj (region c*D floats)
-  float *H = smem + (size_t)c * D;      // c columns, stride sj
-  const float *sig_old = a.X.sig + (size_t)u * r;
+  float *J = smem;                       // c columns, stride sj
+  float *H = smem + lay.j;               // c columns, stride sj
+  const float *sig_old = X.sig + (size_t)u * r;
   if (m == c) {
     for (int idx = tid; idx < c * sj; idx += NT) {
       const int col = idx / sj, row = idx - col * sj;
       float v = 0.f;
-      if (row < m) {
+      if (row < m && col < c) {
         if (row < k)
           v = (row == col) ? sig_old[col] : 0.f;
         else
@@ -239,7 +302,8 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
       J[idx] = v;
     }
   } else {
-    float *Zb = smem;  // m x c column-major
+    float *Zb = smem;  // m x c column-major, column stride mz
+    const int mz = ldz(m);
     for (int idx = tid; idx < m * c; idx += NT) {
       const int col = idx / m, row = idx - col * m;
       float v;
@@ -247,10 +311,10 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
         v = (row == col) ? sig_old[col] : 0.f;
       else
         v = YFP[(row - k) * D + col];
-      Zb[idx] = v;
+      Zb[(size_t)col * mz + row] = v;
     }
     __syncthreads();
-    house_qr(Zb, m, m, c, c, tau);
+    house_qr<2 * D / 4>(Zb, mz, m, c, c, tau);
     // Move R (upper triangle, c x c) into the J layout through registers:
     // the packed upper triangle is dealt evenly over the threads, then the
     // (overlapping) J region is cleared and written.
@@ -264,7 +328,7 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
       if (e < ntri) {
         int col, row;
         tri_index(e, col, row);
-        hold[z] = Zb[(size_t)col * m + row];
+        hold[z] = Zb[(size_t)col * mz + row];
       }
     }
     __syncthreads();
@@ -298,58 +362,65 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
     const float negl = tol * tol * fro2;
     __syncthreads();  // sv is reused below
     const int c2 = c + (c & 1);
+    const int nq4 = rl / 4;  // float4 chunks per quad lane
     int sweep = 0;
     bool conv = (c < 2);
     while (!conv && sweep < SWEEP_CAP) {
       sweep++;
       int rot = 0;
       for (int rnd = 0; rnd < c2 - 1; rnd++) {
-        for (int pr = grp; pr < c2 / 2; pr += 16) {
+        if (qid < c2 / 2) {
           int ci, cj;
-          rr_pair(rnd, pr, c2, ci, cj);
-          if (cj >= c) continue;
-          float *zi = J + (size_t)ci * sj + lane * nj;
-          float *zj = J + (size_t)cj * sj + lane * nj;
-          float xi[8], xj[8];
-          float al = 0.f, be = 0.f, ga = 0.f;
+          rr_pair(rnd, qid, c2, ci, cj);
+          if (cj < c) {
+            float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
+            float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
+            float4 xi[D / 16], xj[D / 16];
+            float al = 0.f, be = 0.f, ga = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; e++) {
-            if (e < nj) {
-              xi[e] = zi[e];
-              xj[e] = zj[e];
-              al += xi[e] * xi[e];
-              be += xj[e] * xj[e];
-              ga += xi[e] * xj[e];
-            }
-          }
-          al = sum16(al);
-          be = sum16(be);
-          ga = sum16(ga);
-          if (al > negl && be > negl && fabsf(ga) > tol * sqrtf(al * be)) {
-            const float zeta = (be - al) / (2.f * ga);
-            const float az = fabsf(zeta);
-            float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
-            t = copysignf(t, zeta);
-            const float cs = 1.f / sqrtf(1.f + t * t);
-            const float sn = cs * t;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-              if (e < nj) {
-                zi[e] = cs * xi[e] - sn * xj[e];
-                zj[e] = sn * xi[e] + cs * xj[e];
+            for (int e = 0; e < D / 16; e++) {
+              if (e < nq4) {
+                xi[e] = zi[e];
+                xj[e] = zj[e];
+                al += xi[e].x * xi[e].x + xi[e].y * xi[e].y + xi[e].z * xi[e].z + xi[e].w * xi[e].w;
+                be += xj[e].x * xj[e].x + xj[e].y * xj[e].y + xj[e].z * xj[e].z + xj[e].w * xj[e].w;
+                ga += xi[e].x * xj[e].x + xi[e].y * xj[e].y + xi[e].z * xj[e].z + xi[e].w * xj[e].w;
               }
             }
-            float *hi = H + (size_t)ci * sj + lane * nj;
-            float *hj = H + (size_t)cj * sj + lane * nj;
+            al = quad_sum(al);
+            be = quad_sum(be);
+            ga = quad_sum(ga);
+            if (al > negl && be > negl && fabsf(ga) > tol * sqrtf(al * be)) {
+              const float zeta = (be - al) / (2.f * ga);
+              const float az = fabsf(zeta);
+              float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
+              t = copysignf(t, zeta);
+              const float cs = 1.f / sqrtf(1.f + t * t);
+              const float sn = cs * t;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-              if (e < nj) {
-                const float p0 = hi[e], p1 = hj[e];
-                hi[e] = cs * p0 - sn * p1;
-                hj[e] = sn * p0 + cs * p1;
+              for (int e = 0; e < D / 16; e++) {
+                if (e < nq4) {
+                  const float4 u0 = xi[e], u1 = xj[e];
+                  zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                                 cs * u0.w - sn * u1.w};
+                  zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                                 sn * u0.w + cs * u1.w};
+                }
               }
+              float4 *hi = (float4 *)(H + (size_t)ci * sj + q * rl);
+              float4 *hj = (float4 *)(H + (size_t)cj * sj + q * rl);
+#pragma unroll
+              for (int e = 0; e < D / 16; e++) {
+                if (e < nq4) {
+                  const float4 u0 = hi[e], u1 = hj[e];
+                  hi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                                 cs * u0.w - sn * u1.w};
+                  hj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                                 sn * u0.w + cs * u1.w};
+                }
+              }
+              rot = 1;
             }
-            rot = 1;
           }
         }
         __syncthreads();
@@ -358,17 +429,17 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
     }
     if (tid == 0) {
       if (!conv) atomicOr(a.status, FLAG_SWEEP_CAP);
-      a.X.sweeps[u] = sweep;
+      X.sweeps[u] = sweep;
     }
   }
 
   // ---------------- phase D: sort, sign, B+, H_top, new rows --------------
-  for (int col = grp; col < c; col += 16) {
-    const float *zc = J + (size_t)col * sj + lane * nj;
+  for (int col = qid; col < c; col += NT / 4) {
+    const float *zc = J + (size_t)col * sj + q * rl;
     float s = 0.f;
-    for (int e = 0; e < nj; e++) s += zc[e] * zc[e];
-    s = sum16(s);
-    if (lane == 0) sv[col] = sqrtf(s);
+    for (int e = 0; e < rl; e++) s += zc[e] * zc[e];
+    s = quad_sum(s);
+    if (q == 0) sv[col] = sqrtf(s);
   }
   __syncthreads();
   // non-finite singular values are flagged and ranked last, so that perm
@@ -394,49 +465,62 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
   }
   __syncthreads();
   {
-    float *sig_new = a.X.sig + (size_t)u * r;
-    // every thread reads the old sigma only in phase B; safe to overwrite now
+    float *sig_new = X.sig + (size_t)u * r;
+    // the old sigma was read only in phase B; safe to overwrite now
     if (tid < r) sig_new[tid] = (tid < kplus) ? sv[perm[tid]] : 0.f;
     if (tid == 0) {
       float dsum = 0.f;
-      for (int q = kplus; q < c; q++) dsum += sv[perm[q]] * sv[perm[q]];
-      a.X.disc[u] = dsum;
+      for (int qq = kplus; qq < c; qq++) dsum += sv[perm[qq]] * sv[perm[qq]];
+      X.disc[u] = dsum;
     }
   }
 
-  // B+ = [B P] H_r into the J region (rows j' x D)
-  __syncthreads();
+  // B+ = [B P] H_r into the J region (rows j' x D), 32 rows at a time
   float *Bp = J;
+  __syncthreads();  // every thread is done with J before B+ overwrites it
   {
     const int cq = tid & 31;  // columns 4cq .. 4cq+3
-    const int rg = tid >> 5;  // rows rg, rg+8, ...
-    constexpr int ZR = D / 8;
-    float acc[ZR][4];
+    const int rg = tid >> 5;  // rows rg, rg+8, rg+16, rg+24 of each chunk
+    for (int j0 = 0; j0 < kplus; j0 += 32) {
+      float acc[4][4];
 #pragma unroll
-    for (int z = 0; z < ZR; z++)
+      for (int z = 0; z < 4; z++)
 #pragma unroll
-      for (int t = 0; t < 4; t++) acc[z][t] = 0.f;
-    for (int i = 0; i < c; i++) {
-      const float *src = (i < k) ? (Bt + (size_t)i * D) : (Pg + (size_t)(i - k) * D);
-      const float4 bp = *reinterpret_cast<const float4 *>(src + 4 * cq);
+        for (int t = 0; t < 4; t++) acc[z][t] = 0.f;
+      for (int i0 = 0; i0 < c; i0 += 8) {
+        float4 bp[8];  // eight rows of [B; P] in flight at once
 #pragma unroll
-      for (int z = 0; z < ZR; z++) {
-        const int jr = rg + 8 * z;
-        if (jr < kplus) {
-          const float hv = H[(size_t)perm[jr] * sj + i];
-          acc[z][0] += hv * bp.x;
-          acc[z][1] += hv * bp.y;
-          acc[z][2] += hv * bp.z;
-          acc[z][3] += hv * bp.w;
+        for (int ii = 0; ii < 8; ii++) {
+          const int i = i0 + ii;
+          bp[ii] = float4{0.f, 0.f, 0.f, 0.f};
+          if (i < c) {
+            const float *src = (i < k) ? (Bt + (size_t)i * D) : (Pg + (size_t)(i - k) * D);
+            bp[ii] = *reinterpret_cast<const float4 *>(src + 4 * cq);
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 8; ii++) {
+          const int i = i0 + ii;
+          if (i < c) {
+#pragma unroll
+            for (int z = 0; z < 4; z++) {
+              const int jr = j0 + rg + 8 * z;
+              if (jr < kplus) {
+                const float hv = H[(size_t)perm[jr] * sj + i];
+                acc[z][0] += hv * bp[ii].x;
+                acc[z][1] += hv * bp[ii].y;
+                acc[z][2] += hv * bp[ii].z;
+                acc[z][3] += hv * bp[ii].w;
+              }
+            }
+          }
         }
       }
-    }
 #pragma unroll
-    for (int z = 0; z < ZR; z++) {
-      const int jr = rg + 8 * z;
-      if (jr < kplus) {
-#pragma unroll
-        for (int t = 0; t < 4; t++) Bp[(size_t)jr * D + 4 * cq + t] = acc[z][t];
+      for (int z = 0; z < 4; z++) {
+        const int jr = j0 + rg + 8 * z;
+        if (jr < kplus)
+          *reinterpret_cast<float4 *>(Bp + (size_t)jr * D + 4 * cq) = float4{acc[z][0], acc[z][1], acc[z][2], acc[z][3]};
       }
     }
   }
@@ -466,12 +550,12 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
   }
   __syncthreads();
   {
-    float *Btw = a.X.Bt + (size_t)u * r * D;
+    float *Btw = X.Bt + (size_t)u * r * D;
     for (int idx = tid; idx < r * D; idx += NT) {
       const int jr = idx / D;
       Btw[idx] = (jr < kplus) ? sgn[jr] * Bp[idx] : 0.f;
     }
-    float *Ht = a.X.Htop + (size_t)u * r * r;
+    float *Ht = X.Htop + (size_t)u * r * r;
     for (int idx = tid; idx < k * kplus; idx += NT) {
       const int i = idx / kplus, jr = idx - i * kplus;
       Ht[(size_t)i * r + jr] = sgn[jr] * H[(size_t)perm[jr] * sj + i];
@@ -486,7 +570,7 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
   }
   __syncthreads();
   {
-    TC *Cn = (TC *)a.X.C + ((size_t)u * a.ncap + a.n) * r;
+    TC *Cn = (TC *)X.C + ((size_t)u * a.ncap + a.n) * r;
     for (int idx = tid; idx < b * r; idx += NT) {
       const int i = idx / r, jr = idx - i * r;
       float s = 0.f;
@@ -502,13 +586,24 @@ __global__ void __launch_bounds__(NT) k_core(const FoldArgs a) {
 }
 
 template <int NR, typename TK, typename TC>
+__global__ void __launch_bounds__(NT, 2) k_core(const FoldArgs a) {
+  extern __shared__ float smem[];
+  if (blockIdx.y == 0)
+    core_body<NR, TK, TC, 0>(a, smem);
+  else
+    core_body<NR, TK, TC, 1>(a, smem);
+}
+
+template <int NR, typename TK, typename TC>
 hipError_t launch_core_t(const FoldArgs &a, int nunits, hipStream_t s) {
-  const size_t lds = core_lds_bytes(a.k, a.b, a.r);
+  size_t lds = core_lds_bytes(a.k[0], a.b, a.r[0]);
+  const size_t lv = core_lds_bytes(a.k[1], a.b, a.r[1]);
+  if (lv > lds) lds = lv;
   auto kern = k_core<NR, TK, TC>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nunits), dim3(NT), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(nunits, 2), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -524,13 +619,12 @@ hipError_t launch_core_nr(const FoldArgs &a, int nunits, hipStream_t s) {
 }  // namespace
 
 size_t core_lds_bytes(int k, int b, int r) {
-  (void)r;
-  return sizeof(float) * ((size_t)core_phase_floats(k, b, r) + 4 * D + 8);
+  return sizeof(float) * ((size_t)core_lds(k, b, r).total + 4 * D);
 }
 
 hipError_t launch_core(const FoldArgs &a0, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
   FoldArgs a = a0;
-  a.lds_small = core_phase_floats(a.k, a.b, a.r);
+  for (int x = 0; x < 2; x++) a.lds_small[x] = core_lds(a.k[x], a.b, a.r[x]).total;
   if (kv_bf16 && coord_bf16) return launch_core_nr<uint16_t, uint16_t>(a, nunits, s);
   if (kv_bf16 && !coord_bf16) return launch_core_nr<uint16_t, float>(a, nunits, s);
   if (!kv_bf16 && coord_bf16) return launch_core_nr<float, uint16_t>(a, nunits, s);

@@ -17,20 +17,23 @@ namespace {
 
 constexpr int TILE = 64;  // rows per workgroup iteration
 
-template <typename TC>
-__global__ void __launch_bounds__(NT) k_rewrite_vec(const RewriteArgs a) {
-  extern __shared__ float sm[];
-  const int k = a.k, kp = a.kp, r = a.r;
+// XK (0 keys, 1 values) is a template constant so that every access to the
+// kernel arguments has a constant offset.
+template <typename TC, int XK>
+__device__ __forceinline__ void rewrite_body(const RewriteArgs &a, float *sm) {
+  const Stream &X = a.X[XK];
+  const int k = a.k[XK], kp = a.kp[XK], r = a.r[XK];
+  if (a.n <= 0 || k <= 0) return;
   const int ldx = k + 1;  // padded row stride of the staged tile
   float *Hs = sm;                    // k x kp
   float *Xs = sm + (size_t)k * kp;   // TILE x ldx
   const int u = a.u0 + blockIdx.y;
-  const float *Ht = a.X.Htop + (size_t)u * r * r;
+  const float *Ht = X.Htop + (size_t)u * r * r;
   for (int idx = threadIdx.x; idx < k * kp; idx += NT) {
     const int i = idx / kp, j = idx - i * kp;
     Hs[idx] = Ht[(size_t)i * r + j];
   }
-  TC *C = (TC *)a.X.C + (size_t)u * a.ncap * r;
+  TC *C = (TC *)X.C + (size_t)u * a.ncap * r;
   const int row_l = threadIdx.x & (TILE - 1);
   const int cg = threadIdx.x / TILE;  // 4 column groups
   for (int t0 = blockIdx.x * TILE; t0 < a.n; t0 += gridDim.x * TILE) {
@@ -66,14 +69,27 @@ __global__ void __launch_bounds__(NT) k_rewrite_vec(const RewriteArgs a) {
   }
 }
 
+template <typename TC>
+__global__ void __launch_bounds__(NT) k_rewrite_vec(const RewriteArgs a) {
+  extern __shared__ float sm[];
+  if (blockIdx.z == 0)
+    rewrite_body<TC, 0>(a, sm);
+  else
+    rewrite_body<TC, 1>(a, sm);
+}
+
 }  // namespace
 
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s) {
   if (a.n <= 0 || nunits <= 0) return hipSuccess;
-  const size_t lds = sizeof(float) * ((size_t)a.k * a.kp + (size_t)TILE * (a.k + 1));
+  size_t lds = 0;
+  for (int x = 0; x < 2; x++) {
+    const size_t l = sizeof(float) * ((size_t)a.k[x] * a.kp[x] + (size_t)TILE * (a.k[x] + 1));
+    if (l > lds) lds = l;
+  }
   int tiles = (a.n + TILE - 1) / TILE;
   if (tiles > 64) tiles = 64;
-  dim3 grid(tiles, nunits);
+  dim3 grid(tiles, nunits, 2);
   if (coord_bf16) {
     hipError_t e = hipFuncSetAttribute((const void *)k_rewrite_vec<uint16_t>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
