@@ -316,21 +316,64 @@ __device__ __forceinline__ void wave_fence() {
 
 __host__ __device__ __forceinline__ int tile_stride(int rsV) { return ((rsV + 15) / 16) * 16 + 4; }
 
-// One 1024-thread workgroup per unit: wavefronts 0..nhw-1 stream the history
-// rows (MFMA scores and values, online softmax), the last wavefront does the
-// window rows when there are any; the waves are combined in LDS and the
-// workgroup writes the unit's outputs. No workgroup talks to another, so no
-// device-scope fence is needed (on a multi-XCD part each one writes back and
-// invalidates the XCD's L2).
+// One 1024-thread workgroup per unit. Every wavefront streams a contiguous
+// slice of the history rows (MFMA scores and values, online softmax, the
+// next 32-row step's loads in flight while the current one is computed) and
+// then a share of the window rows (16 lanes per 128-wide row); the partials
+// of all waves are combined in LDS and the workgroup writes the unit's
+// outputs. No workgroup talks to another, so no device-scope fence is needed
+// (on a multi-XCD part each one writes back and invalidates the XCD's L2).
 constexpr int NTU = 1024;
 constexpr int NWU = NTU / 64;
 constexpr int WH = 2;  // window heads per pass (register budget: 128 VGPRs per lane)
 
-__host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV) {
+__host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV, int g) {
   const size_t qs = (size_t)MAXG * (rsK > 0 ? rsK : 1) + 4 * 64 * 2 * 4;  // q' + fragments
-  const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;  // floats
-  const size_t comb = (size_t)NWU * MAXG * (2 + rsV) + (size_t)MAXG * (2 + D) + (size_t)MAXG * rsV + 8 * MAXG;
+  const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;      // floats
+  const size_t comb = 2 * (size_t)NWU * MAXG + (size_t)NWU * g * rsV + (size_t)NWU * g * (2 + D) +
+                      (size_t)g * rsV + (size_t)g * D + 8 * MAXG;
   return sizeof(float) * (qs + (tiles > comb ? tiles : comb));
+}
+
+template <int KS, int NTV>
+__device__ __forceinline__ void load_step(const uint16_t *CK, const uint16_t *CV, int rsK, int rsV, int rb,
+                                          int we, int lane, u32x4_t *ka, u32x4_t *kb, u32x4_t *vv) {
+  const int hq = lane & 15, qd = lane >> 4;
+  const int cpr = rsV / 8;
+#pragma unroll
+  for (int kc = 0; kc < KS; kc++) {
+    const int col = kc * 32 + 8 * qd;
+    const int r0 = rb + hq, r1 = rb + 16 + hq;
+    ka[kc] = u32x4_t{0u, 0u, 0u, 0u};
+    kb[kc] = u32x4_t{0u, 0u, 0u, 0u};
+    if (col < rsK) {
+      if (r0 < we) ka[kc] = *(const u32x4_t *)(CK + (size_t)r0 * rsK + col);
+      if (r1 < we) kb[kc] = *(const u32x4_t *)(CK + (size_t)r1 * rsK + col);
+    }
+  }
+  // the 32-row C_V tile: 32 x rsV/8 chunks of 16 bytes; 64 * NTV >= 4 * rsV covers them all
+#pragma unroll
+  for (int z = 0; z < NTV; z++) {
+    const int idx = lane + 64 * z;
+    const int rr = idx / cpr, c8 = idx - rr * cpr;
+    vv[z] = u32x4_t{0u, 0u, 0u, 0u};
+    if (idx < 32 * cpr && rb + rr < we) vv[z] = *(const u32x4_t *)(CV + (size_t)(rb + rr) * rsV + c8 * 8);
+  }
+}
+
+template <int NTV>
+__device__ __forceinline__ void store_tile(uint16_t *tile, int ts, int rsV, int lane, const u32x4_t *vv) {
+  const int cpr = rsV / 8;
+#pragma unroll
+  for (int z = 0; z < NTV; z++) {
+    const int idx = lane + 64 * z;
+    const int rr = idx / cpr, c8 = idx - rr * cpr;
+    if (idx < 32 * cpr) {
+      uint2 *dstp = (uint2 *)(tile + rr * ts + c8 * 8);
+      dstp[0] = uint2{vv[z][0], vv[z][1]};
+      dstp[1] = uint2{vv[z][2], vv[z][3]};
+    }
+  }
 }
 
 template <int KS, int NTV>
@@ -339,8 +382,9 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   const int ul = blockIdx.x, u = a.u0 + ul;
   const int g = a.L.g, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rsK = a.L.X[0].r, rsV = a.L.X[1].r;
-  float *qsm = sm;                                  // g x rsK: q'
-  float *big = sm + (size_t)MAXG * rsK + 4 * 64 * 2 * 4;  // after q' and its fragments
+  float *qsm = sm;                                          // g x rsK: q'
+  u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);    // [(kc*2 + part)*64 + lane]
+  float *big = qsm + (size_t)MAXG * rsK + 4 * 64 * 2 * 4;   // tiles, then combine scratch
   int li, bi, h;
   unit_coords(a, ul, li, bi, h);
   const uint16_t *q = (const uint16_t *)a.q + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
@@ -360,9 +404,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  // MFMA B fragments of q' (bf16 hi and lo) per lane, shared by all waves:
-  // frag[(kc * 2 + part) * 64 + lane]
-  u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);
+  // MFMA B fragments of q' (bf16 hi and lo) per lane, shared by all waves
   if (tid < 64 * KS) {
     const int kc = tid >> 6, ln = tid & 63;
     const int fq = ln & 15, fd = ln >> 4;
@@ -375,17 +417,14 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     split8(x, frag[(kc * 2) * 64 + ln], frag[(kc * 2 + 1) * 64 + ln]);
   }
   __syncthreads();
-  const bool has_win = a.e > 0;
-  const int nhw = has_win ? NWU - 1 : NWU;  // history waves
   const int hq = lane & 15, qd = lane >> 4;
-  // per-wave results kept in registers until the loops are done
+  // ---- history rows of this wave ----------------------------------------
   float m = -INFINITY, l = 0.f;
   f32x4_t acc[NTV];
 #pragma unroll
   for (int nt = 0; nt < NTV; nt++) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // window wave results (heads in groups of 4, kept per group in LDS later)
-  if (wv < nhw) {
-    int per = (a.n + nhw - 1) / nhw;
+  {
+    int per = (a.n + NWU - 1) / NWU;
     per = ((per + 31) / 32) * 32;
     const int wb = wv * per;
     const int we = min(a.n, wb + per);
@@ -393,113 +432,115 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.ncap * rsV;
     const int ts = tile_stride(rsV);
     uint16_t *tile = (uint16_t *)big + (size_t)wv * 32 * ts;
-    const int cpr = rsV / 8;
-    for (int rb = wb; rb < we; rb += 32) {
-      // C_K fragments of rows rb..rb+15 and rb+16..rb+31 (issued first)
-      u32x4_t ka[KS], kb[KS];
-#pragma unroll
-      for (int kc = 0; kc < KS; kc++) {
-        const int col = kc * 32 + 8 * qd;
-        const int r0 = rb + hq, r1 = rb + 16 + hq;
-        ka[kc] = u32x4_t{0u, 0u, 0u, 0u};
-        kb[kc] = u32x4_t{0u, 0u, 0u, 0u};
-        if (col < rsK) {
-          if (r0 < we) ka[kc] = *(const u32x4_t *)(CK + (size_t)r0 * rsK + col);
-          if (r1 < we) kb[kc] = *(const u32x4_t *)(CK + (size_t)r1 * rsK + col);
+    // prefetching the next step doubles the load registers: only when they fit
+    constexpr bool PF = (NTV + 2 * KS) <= 6;
+    if (wb < we) {
+      u32x4_t ka[KS], kb[KS], vv[NTV];
+      if constexpr (PF) {
+        load_step<KS, NTV>(CK, CV, rsK, rsV, wb, we, lane, ka, kb, vv);
+        store_tile<NTV>(tile, ts, rsV, lane, vv);
+        wave_fence();
+      }
+      for (int rb = wb; rb < we; rb += 32) {
+        const bool more = rb + 32 < we;
+        u32x4_t nka[KS], nkb[KS], nvv[NTV];
+        if constexpr (PF) {
+          if (more) load_step<KS, NTV>(CK, CV, rsK, rsV, rb + 32, we, lane, nka, nkb, nvv);
+        } else {
+          load_step<KS, NTV>(CK, CV, rsK, rsV, rb, we, lane, ka, kb, vv);
+          store_tile<NTV>(tile, ts, rsV, lane, vv);
+          wave_fence();
         }
-      }
-      // the 32-row C_V tile (32 x rsV/8 chunks of 16 bytes; 64 * NTV >= 4 * rsV)
-      // goes straight to this wave's LDS tile once it has arrived
+        f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int z = 0; z < NTV; z++) {
-        const int idx = lane + 64 * z;
-        const int rr = idx / cpr, c8 = idx - rr * cpr;
-        if (idx < 32 * cpr) {
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (rb + rr < we) v = *(const u32x4_t *)(CV + (size_t)(rb + rr) * rsV + c8 * 8);
-          uint2 *dstp = (uint2 *)(tile + rr * ts + c8 * 8);
-          dstp[0] = uint2{v[0], v[1]};
-          dstp[1] = uint2{v[2], v[3]};
+        for (int kc = 0; kc < KS; kc++) {
+          const u32x4_t bh = frag[(kc * 2) * 64 + lane], bl = frag[(kc * 2 + 1) * 64 + lane];
+          d0 = mfma16(ka[kc], bh, d0);
+          d0 = mfma16(ka[kc], bl, d0);
+          d1 = mfma16(kb[kc], bh, d1);
+          d1 = mfma16(kb[kc], bl, d1);
         }
-      }
-      f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        float s[8];
 #pragma unroll
-      for (int kc = 0; kc < KS; kc++) {
-        const u32x4_t bh = frag[(kc * 2) * 64 + lane], bl = frag[(kc * 2 + 1) * 64 + lane];
-        d0 = mfma16(ka[kc], bh, d0);
-        d0 = mfma16(ka[kc], bl, d0);
-        d1 = mfma16(kb[kc], bh, d1);
-        d1 = mfma16(kb[kc], bl, d1);
-      }
-      float s[8];
+        for (int i = 0; i < 4; i++) {
+          s[i] = (rb + 4 * qd + i < we) ? d0[i] : -INFINITY;
+          s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] : -INFINITY;
+        }
+        float mx = s[0];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        s[i] = (rb + 4 * qd + i < we) ? d0[i] : -INFINITY;
-        s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] : -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; i++) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      const float al = __expf(m - ms);
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        p[i] = __expf(s[i] - ms);
-        ps += p[i];
-      }
-      l = l * al + ps;
-      m = mn;
-#pragma unroll
-      for (int nt = 0; nt < NTV; nt++) acc[nt] *= al;
-      u32x4_t phi, plo;
-      split8(p, phi, plo);
-      wave_fence();
-#pragma unroll
-      for (int nt = 0; nt < NTV; nt++) {
-        const int col = nt * 16 + hq;
-        uint16_t v8[8];
+        for (int i = 1; i < 8; i++) mx = fmaxf(mx, s[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float al = __expf(m - ms);
+        float p[8], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const int row = (i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4);
-          v8[i] = (col < rsV) ? tile[row * ts + col] : (uint16_t)0;
+          p[i] = __expf(s[i] - ms);
+          ps += p[i];
         }
-        const u32x4_t av = {pack2(v8[0], v8[1]), pack2(v8[2], v8[3]), pack2(v8[4], v8[5]), pack2(v8[6], v8[7])};
-        acc[nt] = mfma16(av, phi, acc[nt]);
-        acc[nt] = mfma16(av, plo, acc[nt]);
+        l = l * al + ps;
+        m = mn;
+#pragma unroll
+        for (int nt = 0; nt < NTV; nt++) acc[nt] *= al;
+        u32x4_t phi, plo;
+        split8(p, phi, plo);
+#pragma unroll
+        for (int nt = 0; nt < NTV; nt++) {
+          const int col = nt * 16 + hq;
+          uint16_t v8[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const int row = (i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4);
+            v8[i] = (col < rsV) ? tile[row * ts + col] : (uint16_t)0;
+          }
+          const u32x4_t av = {pack2(v8[0], v8[1]), pack2(v8[2], v8[3]), pack2(v8[4], v8[5]), pack2(v8[6], v8[7])};
+          acc[nt] = mfma16(av, phi, acc[nt]);
+          acc[nt] = mfma16(av, plo, acc[nt]);
+        }
+        wave_fence();
+        if constexpr (PF) {
+          if (more) {
+            store_tile<NTV>(tile, ts, rsV, lane, nvv);
+#pragma unroll
+            for (int kc = 0; kc < KS; kc++) {
+              ka[kc] = nka[kc];
+              kb[kc] = nkb[kc];
+            }
+          }
+          wave_fence();
+        }
       }
-      wave_fence();
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
   }
   __syncthreads();  // tiles are free from here on
   float *hm = big;                                  // [NWU][MAXG] max
   float *hl = hm + NWU * MAXG;                      // [NWU][MAXG] sum
-  float *ha = hl + NWU * MAXG;                      // [NWU][MAXG][rsV] o'
-  float *wo = ha + (size_t)NWU * MAXG * rsV;        // [MAXG][2 + D] window (m, l, o)
-  float *op = wo + (size_t)MAXG * (2 + D);          // [MAXG][rsV] merged o'
-  float *fac = op + (size_t)MAXG * rsV;             // [MAXG][8]: M, L, window factor
-  if (wv < nhw) {
-    if (hq < g) {
-      if (qd == 0) {
-        hm[wv * MAXG + hq] = m;
-        hl[wv * MAXG + hq] = l;
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTV; nt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int col = nt * 16 + 4 * qd + i;
-          if (col < rsV) ha[((size_t)wv * MAXG + hq) * rsV + col] = acc[nt][i];
-        }
+  float *ha = hl + NWU * MAXG;                      // [NWU][g][rsV] o'
+  float *wo = ha + (size_t)NWU * g * rsV;           // [NWU][g][2 + D] window (m, l, o)
+  float *op = wo + (size_t)NWU * g * (2 + D);       // [g][rsV] merged o'
+  float *ow = op + (size_t)g * rsV;                 // [g][D] merged window values
+  float *fac = ow + (size_t)g * D;                  // [MAXG][8]: shift, L
+  if (hq < g) {
+    if (qd == 0) {
+      hm[wv * MAXG + hq] = m;
+      hl[wv * MAXG + hq] = l;
     }
-  } else {
-    // window rows: 4 lane groups of 16, 16 lanes per 128-wide row
+#pragma unroll
+    for (int nt = 0; nt < NTV; nt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int col = nt * 16 + 4 * qd + i;
+        if (col < rsV) ha[((size_t)wv * g + hq) * rsV + col] = acc[nt][i];
+      }
+  }
+  // ---- window rows: row i goes to lane group (i mod 64) of the workgroup ----
+  {
     const int l16 = lane & 15, grp = lane >> 4;
+    const int gg = wv * 4 + grp;
     const uint16_t *kr = (const uint16_t *)a.L.X[0].ring + (size_t)u * a.L.rcap * D;
     const uint16_t *vr = (const uint16_t *)a.L.X[1].ring + (size_t)u * a.L.rcap * D;
     for (int h0 = 0; h0 < g; h0 += WH) {
@@ -514,7 +555,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
           qv[j][t] = (h0 + j < g) ? a.scale * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
         }
       }
-      for (int i = grp; i < a.e; i += 4) {
+      for (int i = gg; i < a.e; i += 4 * NWU) {
         int pos = a.head + i;
         if (pos >= a.L.rcap) pos -= a.L.rcap;
         const u32x4_t kw = *(const u32x4_t *)(kr + (size_t)pos * D + l16 * 8);
@@ -542,6 +583,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
           wm[j] = mn;
         }
       }
+      // combine the 4 lane groups of the wave (xor 16, 32)
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
 #pragma unroll
@@ -564,7 +606,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < WH; j++) {
           if (h0 + j < g) {
-            float *w = wo + (size_t)(h0 + j) * (2 + D);
+            float *w = wo + ((size_t)wv * g + h0 + j) * (2 + D);
             if (l16 == 0) {
               w[0] = wm[j];
               w[1] = wl[j];
@@ -577,40 +619,55 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  // combine: per head the global max M, the sum L and the window factor
+  // ---- combine all waves: per head the max, the sum, o' and window values ---
   if (tid < g) {
-    float M = has_win ? wo[tid * (2 + D)] : -INFINITY;
-    for (int w = 0; w < nhw; w++) M = fmaxf(M, hm[w * MAXG + tid]);
+    float M = -INFINITY;
+    for (int w = 0; w < NWU; w++) {
+      M = fmaxf(M, hm[w * MAXG + tid]);
+      M = fmaxf(M, wo[((size_t)w * g + tid) * (2 + D)]);
+    }
     const float ms = (M == -INFINITY) ? 0.f : M;
-    float L = has_win ? __expf(wo[tid * (2 + D)] - ms) * wo[tid * (2 + D) + 1] : 0.f;
-    for (int w = 0; w < nhw; w++) L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+    float L = 0.f;
+    for (int w = 0; w < NWU; w++) {
+      L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+      const float *ww = wo + ((size_t)w * g + tid) * (2 + D);
+      L += __expf(ww[0] - ms) * ww[1];
+    }
     fac[tid * 8 + 0] = ms;
     fac[tid * 8 + 1] = L;
-    fac[tid * 8 + 2] = has_win ? __expf(wo[tid * (2 + D)] - ms) : 0.f;
   }
   __syncthreads();
   for (int idx = tid; idx < g * rsV; idx += NTU) {
     const int hh = idx / rsV, j = idx - hh * rsV;
     const float ms = fac[hh * 8];
     float s = 0.f;
-    for (int w = 0; w < nhw; w++) s += __expf(hm[w * MAXG + hh] - ms) * ha[((size_t)w * MAXG + hh) * rsV + j];
+    for (int w = 0; w < NWU; w++) s += __expf(hm[w * MAXG + hh] - ms) * ha[((size_t)w * g + hh) * rsV + j];
     op[idx] = s;
+  }
+  for (int idx = tid; idx < g * D; idx += NTU) {
+    const int hh = idx / D, t = idx - hh * D;
+    const float ms = fac[hh * 8];
+    float s = 0.f;
+    for (int w = 0; w < NWU; w++) {
+      const float *ww = wo + ((size_t)w * g + hh) * (2 + D);
+      s += __expf(ww[0] - ms) * ww[2 + t];
+    }
+    ow[idx] = s;
   }
   __syncthreads();
   const float *Bv = a.L.X[1].Bt + (size_t)u * rsV * D;
   float *out = (float *)a.out + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
   for (int idx = tid; idx < g * D; idx += NTU) {
     const int hh = idx / D, t = idx - hh * D;
-    float s = 0.f;
+    float s = ow[idx];
     for (int j = 0; j < a.kV; j++) s += op[hh * rsV + j] * Bv[(size_t)j * D + t];
-    if (has_win) s += fac[hh * 8 + 2] * wo[(size_t)hh * (2 + D) + 2 + t];
     out[idx] = s / fac[hh * 8 + 1];
   }
 }
 
 template <int KS, int NTV>
 hipError_t launch_bf16_t(const DecodeArgs &a, int nunits, hipStream_t s) {
-  const size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r);
+  const size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g);
   hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
