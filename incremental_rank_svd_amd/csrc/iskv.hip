@@ -68,7 +68,7 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
   if (l.nchunk_max < 1) l.nchunk_max = 1;
   const size_t U = (size_t)l.units;
   const size_t cb = l.coord_bf16 ? 2 : 4, kb = l.kv_bf16 ? 2 : 4;
-  const int pmax = c->block < D ? c->block : D;
+  const int pmax = scratch_rows(c->block, c->rank_k, c->rank_v);
   size_t off = 0;
   auto take = [&](size_t bytes) -> void * {
     void *p = base ? (void *)(base + off) : nullptr;
@@ -156,7 +156,7 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
   a.head = h->head[l0];
   a.ncap = L.ncap;
   a.bmax = L.b;
-  a.pmax = L.b < D ? L.b : D;
+  a.pmax = scratch_rows(L.b, L.X[0].r, L.X[1].r);
   a.status = L.status;
   int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
   if (rc) return rc;

@@ -19,13 +19,22 @@ constexpr uint32_t FLAG_NONFINITE = 0x2u;
 // Device buffers of one stream kind (K or V), all carved from the caller's
 // workspace. Units are ordered [layer][batch][kv_head] so a layer range is a
 // contiguous unit range.
+// Rows of D floats in each unit's fold scratch: the residual basis P
+// (min(b, D) rows), later the two k+ x k+ Gram corrections (2 r^2 floats).
+inline int scratch_rows(int block, int rank_k, int rank_v) {
+  const int rm = rank_k > rank_v ? rank_k : rank_v;
+  const int pr = block < D ? block : D;
+  const int er = (2 * rm * rm + D - 1) / D;
+  return pr > er ? pr : er;
+}
+
 struct Stream {
   void *C;          // [U][ncap][r] coordinates C = U Sigma (coord dtype), zero beyond column k
   float *Bt;        // [U][r][D] basis vectors as rows, zero beyond row k
   float *sig;       // [U][r] singular values, zero beyond k
   void *ring;       // [U][rcap][D] exact window ring (kv dtype)
   float *Htop;      // [U][r][r] scratch: signed, sorted H[0:k, 0:k+] of the last fold
-  float *P;         // [U][min(b, D)][D] scratch: residual basis rows of the last fold
+  float *P;         // [U][scratch_rows][D] scratch: residual basis rows, then the basis Gram correction
   float *YFP;       // [U][bmax][D] scratch: rows [F B | F P] of the last fold
   int32_t *sweeps;  // [U] core sweeps of the last fold
   float *disc;      // [U] energy dropped by the last fold
@@ -55,7 +64,7 @@ struct FoldArgs {
   int n, b;          // history rows, block
   int rcap, head;    // ring capacity and ring index of F's first row
   int ncap, bmax;
-  int pmax;          // rows per unit of the residual-basis scratch, min(b, D)
+  int pmax;          // rows of D floats per unit of the fold scratch (scratch_rows)
   uint32_t *status;
   int lds_small[2];  // float offset of the small arrays in dynamic LDS, per kind
 };

@@ -77,6 +77,26 @@ __device__ __forceinline__ void rr_pair(int rnd, int pr, int c2, int &i, int &j)
   j = a < b ? b : a;
 }
 
+// double-precision quad sum (two 32-bit DPP moves per step)
+__device__ __forceinline__ double dpp_d(double v, int ctrl_xor1) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const int lo = (int)(u & 0xffffffffull), hi = (int)(u >> 32);
+  int lo2, hi2;
+  if (ctrl_xor1) {
+    lo2 = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+    hi2 = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false);
+  } else {
+    lo2 = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+    hi2 = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false);
+  }
+  return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi2 << 32) | (unsigned)lo2);
+}
+__device__ __forceinline__ double quad_sum_d(double v) {
+  v += dpp_d(v, 1);
+  v += dpp_d(v, 0);
+  return v;
+}
+
 // sum over the 4 lanes of a quad (DPP quad permutations, no LDS traffic)
 __device__ __forceinline__ float quad_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
@@ -358,8 +378,15 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     if ((tid & 63) == 0) sv[tid >> 6] = fr;
     __syncthreads();
     const float fro2 = sv[0] + sv[1] + sv[2] + sv[3];
-    const float tol = (float)c * 5.9604645e-8f;  // c * 2^-24
-    const float negl = tol * tol * fro2;
+    // Column dot products are accumulated in fp64 (full rate on this part),
+    // so a pair is rotated while its cosine exceeds 8 * 2^-24: just above what
+    // rotating fp32 columns can reach, far below the c * 2^-24 a fp32 dot
+    // product could resolve. Each fold then leaves its stored coordinates
+    // orthogonal to a few fp32 ulps instead of c ulps, which is what keeps
+    // hundreds of successive folds on the exact-arithmetic trajectory.
+    const double tol = 8.0 * 5.9604644775390625e-8;
+    const float ntol = (float)c * 5.9604645e-8f;  // columns below ntol * ||J|| are rounding noise
+    const double negl = (double)(ntol * ntol * fro2);
     __syncthreads();  // sv is reused below
     const int c2 = c + (c & 1);
     const int nq4 = rl / 4;  // float4 chunks per quad lane
@@ -376,27 +403,30 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
             float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
             float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
             float4 xi[D / 16], xj[D / 16];
-            float al = 0.f, be = 0.f, ga = 0.f;
+            double al = 0.0, be = 0.0, ga = 0.0;
 #pragma unroll
             for (int e = 0; e < D / 16; e++) {
               if (e < nq4) {
                 xi[e] = zi[e];
                 xj[e] = zj[e];
-                al += xi[e].x * xi[e].x + xi[e].y * xi[e].y + xi[e].z * xi[e].z + xi[e].w * xi[e].w;
-                be += xj[e].x * xj[e].x + xj[e].y * xj[e].y + xj[e].z * xj[e].z + xj[e].w * xj[e].w;
-                ga += xi[e].x * xj[e].x + xi[e].y * xj[e].y + xi[e].z * xj[e].z + xi[e].w * xj[e].w;
+                const double a0 = xi[e].x, a1 = xi[e].y, a2 = xi[e].z, a3 = xi[e].w;
+                const double b0 = xj[e].x, b1 = xj[e].y, b2 = xj[e].z, b3 = xj[e].w;
+                al += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
+                be += b0 * b0 + b1 * b1 + b2 * b2 + b3 * b3;
+                ga += a0 * b0 + a1 * b1 + a2 * b2 + a3 * b3;
               }
             }
-            al = quad_sum(al);
-            be = quad_sum(be);
-            ga = quad_sum(ga);
-            if (al > negl && be > negl && fabsf(ga) > tol * sqrtf(al * be)) {
-              const float zeta = (be - al) / (2.f * ga);
-              const float az = fabsf(zeta);
-              float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
-              t = copysignf(t, zeta);
-              const float cs = 1.f / sqrtf(1.f + t * t);
-              const float sn = cs * t;
+            al = quad_sum_d(al);
+            be = quad_sum_d(be);
+            ga = quad_sum_d(ga);
+            if (al > negl && be > negl && fabs(ga) > tol * sqrt(al * be)) {
+              const double zeta = (be - al) / (2.0 * ga);
+              const double az = fabs(zeta);
+              double td = (az > 1e150) ? 0.5 / az : 1.0 / (az + sqrt(1.0 + az * az));
+              td = copysign(td, zeta);
+              const double csd = 1.0 / sqrt(1.0 + td * td);
+              const float cs = (float)csd;
+              const float sn = (float)(csd * td);
 #pragma unroll
               for (int e = 0; e < D / 16; e++) {
                 if (e < nq4) {
@@ -434,6 +464,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
   }
 
   // ---------------- phase D: sort, sign, B+, H_top, new rows --------------
+  if (tid < k) tau[tid] = sig_old[tid];  // tau is dead after phase B; sigma is rewritten below
   for (int col = qid; col < c; col += NT / 4) {
     const float *zc = J + (size_t)col * sj + q * rl;
     float s = 0.f;
@@ -549,39 +580,142 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     if (lane == 0) sgn[jr] = (Bp[(size_t)jr * D + bi] < 0.f) ? -1.f : 1.f;
   }
   __syncthreads();
-  {
-    float *Btw = X.Bt + (size_t)u * r * D;
-    for (int idx = tid; idx < r * D; idx += NT) {
-      const int jr = idx / D;
-      Btw[idx] = (jr < kplus) ? sgn[jr] * Bp[idx] : 0.f;
+  // Re-orthonormalization. In exact arithmetic B+ has orthonormal rows and
+  // H is orthogonal; in fp32 each fold leaves errors of a few ulps, and B+
+  // inherits the previous basis's error, so uncorrected the basis drifts
+  // linearly with the number of folds. Two Gram errors are measured:
+  //   E   = B+ B+^T - I      (everything: H and the basis [B P])
+  //   E_H = H_r^T H_r - I    (the accumulated rotations alone).
+  // (I - E/2) B+ is orthonormal to O(E^2). A rotation error inflates C+ = Z H_r
+  // and B+ alike, so it is removed from both sides (factor I - E_H/2); a basis
+  // error belongs to the coordinates, which take the inverse factor of its
+  // share. C+ therefore takes G = I + E/2 - E_H, and sigma its diagonal, so
+  // the stored sigma stays the column norms of the stored coordinates.
+  // Both matrices live in the fold scratch, which is dead once B+ is formed.
+  for (int idx = tid; idx < kplus * D; idx += NT) Bp[idx] *= sgn[idx / D];
+  __syncthreads();
+  float *Eg = Pg;                             // kplus x kplus: E
+  float *Gg = Pg + (size_t)kplus * kplus;     // kplus x kplus: E/2 - E_H
+  for (int e = tid; e < kplus * kplus; e += NT) {
+    const int i = e / kplus, j = e - i * kplus;
+    const float *bi = Bp + (size_t)i * D, *bj = Bp + (size_t)j * D;
+    double acc = 0.0;
+    for (int t = 0; t < D / 4; t++) {
+      const int v = 4 * ((t + i + j) & (D / 4 - 1));  // rotate the start: fewer bank conflicts
+      const float4 x = *reinterpret_cast<const float4 *>(bi + v);
+      const float4 y = *reinterpret_cast<const float4 *>(bj + v);
+      acc += (double)x.x * y.x + (double)x.y * y.y + (double)x.z * y.z + (double)x.w * y.w;
     }
-    float *Ht = X.Htop + (size_t)u * r * r;
-    for (int idx = tid; idx < k * kplus; idx += NT) {
-      const int i = idx / kplus, jr = idx - i * kplus;
-      Ht[(size_t)i * r + jr] = sgn[jr] * H[(size_t)perm[jr] * sj + i];
+    const float *hi = H + (size_t)perm[i] * sj, *hj = H + (size_t)perm[j] * sj;
+    double ah = 0.0;
+    for (int l = 0; l < c; l++) ah += (double)hi[l] * hj[l];
+    ah *= (double)(sgn[i] * sgn[j]);
+    const double dl = (i == j) ? 1.0 : 0.0;
+    Eg[e] = (float)(acc - dl);
+    Gg[e] = (float)(0.5 * (acc - dl) - (ah - dl));
+  }
+  __syncthreads();
+  {
+    // B = (I - E/2) B+ straight to the output basis; lanes own columns, so
+    // every E entry a wave reads is uniform across it
+    const int wv = tid >> 6, ln = tid & 63;
+    float *Btw = X.Bt + (size_t)u * r * D;
+    for (int i0 = 4 * wv; i0 < kplus; i0 += 16) {
+      float acc[4][2];
+#pragma unroll
+      for (int z = 0; z < 4; z++) acc[z][0] = acc[z][1] = 0.f;
+      for (int l = 0; l < kplus; l++) {
+        const float b0 = Bp[(size_t)l * D + ln], b1 = Bp[(size_t)l * D + ln + 64];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const float ev = (i0 + z < kplus) ? Eg[(size_t)(i0 + z) * kplus + l] : 0.f;
+          acc[z][0] += ev * b0;
+          acc[z][1] += ev * b1;
+        }
+      }
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        const int i = i0 + z;
+        if (i < kplus) {
+          Btw[(size_t)i * D + ln] = Bp[(size_t)i * D + ln] - 0.5f * acc[z][0];
+          Btw[(size_t)i * D + ln + 64] = Bp[(size_t)i * D + ln + 64] - 0.5f * acc[z][1];
+        }
+      }
+    }
+    for (int idx = kplus * D + tid; idx < r * D; idx += NT) Btw[idx] = 0.f;
+  }
+  __syncthreads();  // B+ in the J region is dead from here on
+  // Hn = H_r G, signs and rank order applied, column-major (stride sj)
+  float *Hn = J;
+  {
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int j0 = 4 * wv; j0 < kplus; j0 += 16) {
+      for (int i = ln; i < c; i += 64) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int l = 0; l < kplus; l++) {
+          const float hv = sgn[l] * H[(size_t)perm[l] * sj + i];
+#pragma unroll
+          for (int z = 0; z < 4; z++)
+            if (j0 + z < kplus) acc[z] += hv * Gg[(size_t)l * kplus + j0 + z];
+        }
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const int jr = j0 + z;
+          if (jr < kplus) Hn[(size_t)jr * sj + i] = sgn[jr] * H[(size_t)perm[jr] * sj + i] + acc[z];
+        }
+      }
     }
   }
   __syncthreads();
-  // new rows C[n + i] = [F B | F P]_i H_r (b x k+), staged through LDS
-  float *Ys = J;  // b x c, row stride c
+  {
+    float *Ht = X.Htop + (size_t)u * r * r;
+    for (int idx = tid; idx < k * kplus; idx += NT) {
+      const int i = idx / kplus, jr = idx - i * kplus;
+      Ht[(size_t)i * r + jr] = Hn[(size_t)jr * sj + i];
+    }
+  }
+  // new rows C[n + i] = [F B | F P]_i Hn (b x k+), staged through the H region
+  float *Ys = H;  // b x c, row stride c (b * c <= c * sj)
   for (int idx = tid; idx < b * c; idx += NT) {
     const int i = idx / c, l = idx - i * c;
     Ys[idx] = YFP[(size_t)i * D + l];
   }
   __syncthreads();
+  // Each thread owns one column and a strided set of rows, so the squared
+  // column norms of the new rows reduce in a fixed order.
+  float *part = sv;  // ngrp x r partial sums (sv and sgn are dead here)
+  const int ngrp = NT / r;
   {
     TC *Cn = (TC *)X.C + ((size_t)u * a.ncap + a.n) * r;
-    for (int idx = tid; idx < b * r; idx += NT) {
-      const int i = idx / r, jr = idx - i * r;
-      float s = 0.f;
-      if (jr < kplus) {
-        const float *hc = H + (size_t)perm[jr] * sj;
-        const float *yr = Ys + (size_t)i * c;
-        for (int l = 0; l < c; l++) s += yr[l] * hc[l];
-        s *= sgn[jr];
+    if (tid < ngrp * r) {
+      const int jr = tid % r, g0 = tid / r;
+      float sq = 0.f;
+      for (int i = g0; i < b; i += ngrp) {
+        float s = 0.f;
+        if (jr < kplus) {
+          const float *hc = Hn + (size_t)jr * sj;
+          const float *yr = Ys + (size_t)i * c;
+          for (int l = 0; l < c; l++) s += yr[l] * hc[l];
+        }
+        stf<TC>(Cn, (size_t)i * r + jr, s);
+        sq += s * s;
       }
-      stf<TC>(Cn, (size_t)i * r + jr, s);
+      part[g0 * r + jr] = sq;
     }
+  }
+  __syncthreads();
+  // sigma = column norms of the stored coordinates: rewritten old rows
+  // (orthogonal columns of norms sigma_old, so sum_l sigma_l^2 Hn[l][j]^2)
+  // plus the new rows. Computing it from what is stored keeps the next
+  // fold's Z an exact description of the stored history.
+  if (tid < r) {
+    float s2 = 0.f;
+    if (tid < kplus) {
+      const float *hc = Hn + (size_t)tid * sj;
+      for (int l = 0; l < k; l++) s2 += (tau[l] * hc[l]) * (tau[l] * hc[l]);
+      for (int g = 0; g < ngrp; g++) s2 += part[g * r + tid];
+    }
+    X.sig[(size_t)u * r + tid] = sqrtf(s2);
   }
 }
 
