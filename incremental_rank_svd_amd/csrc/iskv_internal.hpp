@@ -90,6 +90,7 @@ struct DecodeArgs {
   int n, e, kK, kV, head;
   int nchunk;
   float scale;
+  int wlds;  // window rows staged in LDS (set by the launcher)
 };
 
 // ---------------------------------------------------------------------------

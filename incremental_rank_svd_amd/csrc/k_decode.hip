@@ -327,12 +327,28 @@ constexpr int NTU = 1024;
 constexpr int NWU = NTU / 64;
 constexpr int WH = 2;  // window heads per pass (register budget: 128 VGPRs per lane)
 
-__host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV, int g) {
-  const size_t qs = (size_t)MAXG * (rsK > 0 ? rsK : 1) + 4 * 64 * 2 * 4;  // q' + fragments
-  const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;      // floats
+// LDS in floats: q' and its fragments, then the per-wave tiles (history) or
+// the combine scratch, then (optionally) the window rows, K then V, bf16.
+__host__ __device__ inline size_t decode_unit_qs(int rsK) {
+  return (size_t)MAXG * (rsK > 0 ? rsK : 1) + 4 * 64 * 2 * 4 + 4 * 64 * 4;  // q', its fragments, q fragments
+}
+__host__ __device__ inline size_t decode_unit_big(int rsV, int g) {
+  const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;
   const size_t comb = 2 * (size_t)NWU * MAXG + (size_t)NWU * g * rsV + (size_t)NWU * g * (2 + D) +
                       (size_t)g * rsV + (size_t)g * D + 8 * MAXG;
-  return sizeof(float) * (qs + (tiles > comb ? tiles : comb));
+  return tiles > comb ? tiles : comb;
+}
+__host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV, int g, int ewin) {
+  return sizeof(float) * (decode_unit_qs(rsK) + decode_unit_big(rsV, g) + (size_t)ewin * D);
+}
+
+// Window rows of the workgroup's window share: from the LDS copy or the ring.
+template <bool STAGED>
+__device__ __forceinline__ const uint16_t *win_row(const uint16_t *base, int i, int head, int rcap) {
+  if (STAGED) return base + (size_t)i * D;
+  int pos = head + i;
+  if (pos >= rcap) pos -= rcap;
+  return base + (size_t)pos * D;
 }
 
 template <int KS, int NTV>
@@ -376,6 +392,169 @@ __device__ __forceinline__ void store_tile(uint16_t *tile, int ts, int rsV, int 
   }
 }
 
+// Window rows of one unit straight from the ring (used when the window does
+// not fit in LDS): row i goes to lane group (i mod 64) of the workgroup (16
+// lanes per 128-wide row), WH heads per pass, online softmax; the 4 lane
+// groups of a wave are combined with shuffles and each wave leaves (max, sum,
+// values) per head in wo.
+__device__ __forceinline__ void window_part(const DecodeArgs &a, const uint16_t *q, const uint16_t *kr,
+                                            const uint16_t *vr, float *wo, int g, int wv, int lane) {
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int gg = wv * 4 + grp;
+  for (int h0 = 0; h0 < g; h0 += WH) {
+    float qv[WH][8], wa[WH][8], wm[WH], wl[WH];
+#pragma unroll
+    for (int j = 0; j < WH; j++) {
+      wm[j] = -INFINITY;
+      wl[j] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        wa[j][t] = 0.f;
+        qv[j][t] = (h0 + j < g) ? a.scale * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
+      }
+    }
+    for (int i = gg; i < a.e; i += 4 * NWU) {
+      const u32x4_t kw = *(const u32x4_t *)(win_row<false>(kr, i, a.head, a.L.rcap) + l16 * 8);
+      const u32x4_t vw = *(const u32x4_t *)(win_row<false>(vr, i, a.head, a.L.rcap) + l16 * 8);
+      float kx[8], vx[8];
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        kx[2 * t] = __uint_as_float(kw[t] << 16);
+        kx[2 * t + 1] = __uint_as_float(kw[t] & 0xffff0000u);
+        vx[2 * t] = __uint_as_float(vw[t] << 16);
+        vx[2 * t + 1] = __uint_as_float(vw[t] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int j = 0; j < WH; j++) {
+        float sc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; t++) sc += kx[t] * qv[j][t];
+        sc = sum16(sc);
+        const float mn = fmaxf(wm[j], sc);
+        const float al = __expf(wm[j] - mn);
+        const float pv = __expf(sc - mn);
+        wl[j] = wl[j] * al + pv;
+#pragma unroll
+        for (int t = 0; t < 8; t++) wa[j][t] = wa[j][t] * al + pv * vx[t];
+        wm[j] = mn;
+      }
+    }
+    // combine the 4 lane groups of the wave (xor 16, 32)
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < WH; j++) {
+        const float mo = __shfl_xor(wm[j], off);
+        const float lo = __shfl_xor(wl[j], off);
+        const float mn = fmaxf(wm[j], mo);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float f0 = __expf(wm[j] - ms), f1 = __expf(mo - ms);
+        wl[j] = wl[j] * f0 + lo * f1;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          const float ao = __shfl_xor(wa[j][t], off);
+          wa[j][t] = wa[j][t] * f0 + ao * f1;
+        }
+        wm[j] = mn;
+      }
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < WH; j++) {
+        if (h0 + j < g) {
+          float *w = wo + ((size_t)wv * g + h0 + j) * (2 + D);
+          if (l16 == 0) {
+            w[0] = wm[j];
+            w[1] = wl[j];
+          }
+#pragma unroll
+          for (int t = 0; t < 8; t++) w[2 + l16 * 8 + t] = wa[j][t];
+        }
+      }
+    }
+  }
+}
+
+// Window rows staged in LDS, on matrix cores: the window is one more
+// history-like stream with 128 key dims (4 K steps, B = q itself, exact in
+// bf16, the scale applied to the fp32 scores) and 128 value columns (8 tiles).
+// Wave wv takes the 32-row steps wv, wv + NWU, ...; every wave leaves its
+// (max, sum, values) per head in wo[wv].
+__device__ __forceinline__ void window_mfma(const DecodeArgs &a, const u32x4_t *qfrag, const uint16_t *wk,
+                                            const uint16_t *wvr, float *wo, int g, int wv, int lane) {
+  const int hq = lane & 15, qd = lane >> 4;
+  const int e = a.e;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; nt++) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 32 * wv; rb < e; rb += 32 * NWU) {
+    f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+    const int r0 = rb + hq, r1 = rb + 16 + hq;
+#pragma unroll
+    for (int kc = 0; kc < 4; kc++) {
+      const int col = kc * 32 + 8 * qd;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t k0 = (r0 < e) ? *(const u32x4_t *)(wk + (size_t)r0 * D + col) : z;
+      const u32x4_t k1 = (r1 < e) ? *(const u32x4_t *)(wk + (size_t)r1 * D + col) : z;
+      const u32x4_t bq = qfrag[kc * 64 + lane];
+      d0 = mfma16(k0, bq, d0);
+      d1 = mfma16(k1, bq, d1);
+    }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      s[i] = (rb + 4 * qd + i < e) ? a.scale * d0[i] : -INFINITY;
+      s[4 + i] = (rb + 16 + 4 * qd + i < e) ? a.scale * d1[i] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float ms = (mn == -INFINITY) ? 0.f : mn;
+    const float al = __expf(m - ms);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      p[i] = __expf(s[i] - ms);
+      ps += p[i];
+    }
+    l = l * al + ps;
+    m = mn;
+    u32x4_t phi, plo;
+    split8(p, phi, plo);
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) {
+      acc[nt] *= al;
+      const int col = nt * 16 + hq;
+      uint16_t v8[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int row = rb + ((i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4));
+        v8[i] = (row < e) ? wvr[(size_t)row * D + col] : (uint16_t)0;
+      }
+      const u32x4_t av = {pack2(v8[0], v8[1]), pack2(v8[2], v8[3]), pack2(v8[4], v8[5]), pack2(v8[6], v8[7])};
+      acc[nt] = mfma16(av, phi, acc[nt]);
+      acc[nt] = mfma16(av, plo, acc[nt]);
+    }
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (hq < g) {
+    float *w = wo + ((size_t)wv * g + hq) * (2 + D);
+    if (qd == 0) {
+      w[0] = m;
+      w[1] = l;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) w[2 + nt * 16 + 4 * qd + i] = acc[nt][i];
+  }
+}
+
 template <int KS, int NTV>
 __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   extern __shared__ float sm[];
@@ -384,10 +563,51 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   const int rsK = a.L.X[0].r, rsV = a.L.X[1].r;
   float *qsm = sm;                                          // g x rsK: q'
   u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);    // [(kc*2 + part)*64 + lane]
-  float *big = qsm + (size_t)MAXG * rsK + 4 * 64 * 2 * 4;   // tiles, then combine scratch
+  u32x4_t *qfrag = frag + 4 * 2 * 64;                        // [kc*64 + lane]: q itself (bf16)
+  float *big = qsm + decode_unit_qs(rsK);                   // tiles, then combine scratch
+  uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g));  // [2][e][D] window copy
   int li, bi, h;
   unit_coords(a, ul, li, bi, h);
   const uint16_t *q = (const uint16_t *)a.q + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
+  const uint16_t *kr = (const uint16_t *)a.L.X[0].ring + (size_t)u * a.L.rcap * D;
+  const uint16_t *vr = (const uint16_t *)a.L.X[1].ring + (size_t)u * a.L.rcap * D;
+  // The window rows are copied to LDS in batches of WB 16-byte chunks per
+  // thread; the first batch's loads are in flight during the q' projection.
+  constexpr int WB = 8;
+  const int wch = a.wlds ? 2 * a.e * (D / 8) : 0;  // K rows, then V rows
+  u32x4_t wbuf[WB];
+  auto win_load = [&](int c0) {
+#pragma unroll
+    for (int z = 0; z < WB; z++) {
+      const int c = c0 + z * NTU + tid;
+      wbuf[z] = u32x4_t{0u, 0u, 0u, 0u};
+      if (c < wch) {
+        const int which = c >= a.e * (D / 8);
+        const int rem = c - which * a.e * (D / 8);
+        const int i = rem >> 4, part = rem & 15;
+        wbuf[z] = *(const u32x4_t *)(win_row<false>(which ? vr : kr, i, a.head, a.L.rcap) + part * 8);
+      }
+    }
+  };
+  auto win_store = [&](int c0) {
+#pragma unroll
+    for (int z = 0; z < WB; z++) {
+      const int c = c0 + z * NTU + tid;
+      if (c < wch) *(u32x4_t *)(wsm + (size_t)c * 8) = wbuf[z];
+    }
+  };
+  if (wch > 0) win_load(0);
+  // this wave's history slice; its first step is loaded before the projection
+  int per = (a.n + NWU - 1) / NWU;
+  per = ((per + 31) / 32) * 32;
+  const int wb = wv * per;
+  const int we = min(a.n, wb + per);
+  const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.ncap * rsK;
+  const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.ncap * rsV;
+  // prefetching the next step doubles the load registers: only when they fit
+  constexpr bool PF = (NTV + 2 * KS) <= 6;
+  u32x4_t ka[KS], kb[KS], vv[NTV];
+  if (PF && wb < we) load_step<KS, NTV>(CK, CV, rsK, rsV, wb, we, lane, ka, kb, vv);
   // q' = scale * B_K^T q, zero beyond the current rank (16 lanes per dot)
   {
     const float *Bt = a.L.X[0].Bt + (size_t)u * rsK * D;
@@ -401,6 +621,20 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       }
       s = sum16(s);
       if (l16 == 0) qsm[hh * rsK + jj] = a.scale * s;
+    }
+  }
+  if (a.wlds && tid < 4 * 64) {
+    // B fragments of q for the window scores: head l % 16, dims 32 kc + 8 (l / 16) .. +7
+    const int kc = tid >> 6, ln = tid & 63, fq = ln & 15;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (fq < g) v = *(const u32x4_t *)(q + (size_t)fq * D + kc * 32 + 8 * (ln >> 4));
+    qfrag[kc * 64 + ln] = v;
+  }
+  if (wch > 0) {
+    win_store(0);
+    for (int c0 = WB * NTU; c0 < wch; c0 += WB * NTU) {
+      win_load(c0);
+      win_store(c0);
     }
   }
   __syncthreads();
@@ -424,20 +658,10 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NTV; nt++) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
-    int per = (a.n + NWU - 1) / NWU;
-    per = ((per + 31) / 32) * 32;
-    const int wb = wv * per;
-    const int we = min(a.n, wb + per);
-    const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.ncap * rsK;
-    const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.ncap * rsV;
     const int ts = tile_stride(rsV);
     uint16_t *tile = (uint16_t *)big + (size_t)wv * 32 * ts;
-    // prefetching the next step doubles the load registers: only when they fit
-    constexpr bool PF = (NTV + 2 * KS) <= 6;
     if (wb < we) {
-      u32x4_t ka[KS], kb[KS], vv[NTV];
       if constexpr (PF) {
-        load_step<KS, NTV>(CK, CV, rsK, rsV, wb, we, lane, ka, kb, vv);
         store_tile<NTV>(tile, ts, rsV, lane, vv);
         wave_fence();
       }
@@ -538,86 +762,10 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       }
   }
   // ---- window rows: row i goes to lane group (i mod 64) of the workgroup ----
-  {
-    const int l16 = lane & 15, grp = lane >> 4;
-    const int gg = wv * 4 + grp;
-    const uint16_t *kr = (const uint16_t *)a.L.X[0].ring + (size_t)u * a.L.rcap * D;
-    const uint16_t *vr = (const uint16_t *)a.L.X[1].ring + (size_t)u * a.L.rcap * D;
-    for (int h0 = 0; h0 < g; h0 += WH) {
-      float qv[WH][8], wa[WH][8], wm[WH], wl[WH];
-#pragma unroll
-      for (int j = 0; j < WH; j++) {
-        wm[j] = -INFINITY;
-        wl[j] = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; t++) {
-          wa[j][t] = 0.f;
-          qv[j][t] = (h0 + j < g) ? a.scale * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
-        }
-      }
-      for (int i = gg; i < a.e; i += 4 * NWU) {
-        int pos = a.head + i;
-        if (pos >= a.L.rcap) pos -= a.L.rcap;
-        const u32x4_t kw = *(const u32x4_t *)(kr + (size_t)pos * D + l16 * 8);
-        const u32x4_t vw = *(const u32x4_t *)(vr + (size_t)pos * D + l16 * 8);
-        float kx[8], vx[8];
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          kx[2 * t] = __uint_as_float(kw[t] << 16);
-          kx[2 * t + 1] = __uint_as_float(kw[t] & 0xffff0000u);
-          vx[2 * t] = __uint_as_float(vw[t] << 16);
-          vx[2 * t + 1] = __uint_as_float(vw[t] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int j = 0; j < WH; j++) {
-          float sc = 0.f;
-#pragma unroll
-          for (int t = 0; t < 8; t++) sc += kx[t] * qv[j][t];
-          sc = sum16(sc);
-          const float mn = fmaxf(wm[j], sc);
-          const float al = __expf(wm[j] - mn);
-          const float pv = __expf(sc - mn);
-          wl[j] = wl[j] * al + pv;
-#pragma unroll
-          for (int t = 0; t < 8; t++) wa[j][t] = wa[j][t] * al + pv * vx[t];
-          wm[j] = mn;
-        }
-      }
-      // combine the 4 lane groups of the wave (xor 16, 32)
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < WH; j++) {
-          const float mo = __shfl_xor(wm[j], off);
-          const float lo = __shfl_xor(wl[j], off);
-          const float mn = fmaxf(wm[j], mo);
-          const float ms = (mn == -INFINITY) ? 0.f : mn;
-          const float f0 = __expf(wm[j] - ms), f1 = __expf(mo - ms);
-          wl[j] = wl[j] * f0 + lo * f1;
-#pragma unroll
-          for (int t = 0; t < 8; t++) {
-            const float ao = __shfl_xor(wa[j][t], off);
-            wa[j][t] = wa[j][t] * f0 + ao * f1;
-          }
-          wm[j] = mn;
-        }
-      }
-      if (grp == 0) {
-#pragma unroll
-        for (int j = 0; j < WH; j++) {
-          if (h0 + j < g) {
-            float *w = wo + ((size_t)wv * g + h0 + j) * (2 + D);
-            if (l16 == 0) {
-              w[0] = wm[j];
-              w[1] = wl[j];
-            }
-#pragma unroll
-            for (int t = 0; t < 8; t++) w[2 + l16 * 8 + t] = wa[j][t];
-          }
-        }
-      }
-    }
-  }
+  if (a.wlds)
+    window_mfma(a, qfrag, wsm, wsm + (size_t)a.e * D, wo, g, wv, lane);
+  else
+    window_part(a, q, kr, vr, wo, g, wv, lane);
   __syncthreads();
   // ---- combine all waves: per head the max, the sum, o' and window values ---
   if (tid < g) {
@@ -666,8 +814,12 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
 }
 
 template <int KS, int NTV>
-hipError_t launch_bf16_t(const DecodeArgs &a, int nunits, hipStream_t s) {
-  const size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g);
+hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
+  DecodeArgs a = a0;
+  // stage the window in LDS when it fits next to the rest (160 KB per workgroup)
+  size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, a.e);
+  a.wlds = (a.e > 0 && lds <= 160 * 1024 && ((uintptr_t)a.q & 15) == 0) ? 1 : 0;
+  if (!a.wlds) lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, 0);
   hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

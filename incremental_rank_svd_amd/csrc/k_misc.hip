@@ -7,28 +7,28 @@ namespace {
 
 // Copy nrows new rows per unit into the window ring (section "Architecture
 // Overview": the most recent rows are kept exactly). blockIdx.y selects K/V.
-// One thread moves 4 bytes.
-__global__ void __launch_bounds__(NT) k_ingest(const IngestArgs a, int elem_bytes) {
-  const int which = blockIdx.y;
-  const int words_per_row = D * elem_bytes / 4;
-  const size_t total = (size_t)a.batch * a.nl * a.kvh * a.nrows * words_per_row;
-  const uint32_t *src = (const uint32_t *)a.src[which];
-  uint32_t *ring = (uint32_t *)a.ring[which];
-  for (size_t idx = (size_t)blockIdx.x * NT + threadIdx.x; idx < total; idx += (size_t)gridDim.x * NT) {
-    const int wd = (int)(idx % words_per_row);
-    size_t t = idx / words_per_row;
-    const int i = (int)(t % a.nrows);
-    t /= a.nrows;
-    const int h = (int)(t % a.kvh);
-    t /= a.kvh;
-    const int li = (int)(t % a.nl);
-    const int bi = (int)(t / a.nl);
-    const size_t s_off =
-        ((((size_t)bi * a.nl_in + a.lrel0 + li) * a.kvh + h) * a.nrows + i) * words_per_row + wd;
+// A row is moved by words_per_row consecutive threads (16-byte words when
+// the source is 16-byte aligned), so the index arithmetic is per row.
+template <typename W>
+__global__ void __launch_bounds__(NT) k_ingest(const IngestArgs a, int words_per_row) {
+  const W *src = (const W *)a.src[blockIdx.y];
+  W *ring = (W *)a.ring[blockIdx.y];
+  const int rows = a.batch * a.nl * a.kvh * a.nrows;
+  const int rows_per_blk = NT / words_per_row;  // words_per_row divides NT
+  const int wd = threadIdx.x % words_per_row, rl = threadIdx.x / words_per_row;
+  for (int t = blockIdx.x * rows_per_blk + rl; t < rows; t += gridDim.x * rows_per_blk) {
+    int x = t;
+    const int i = x % a.nrows;
+    x /= a.nrows;
+    const int h = x % a.kvh;
+    x /= a.kvh;
+    const int li = x % a.nl;
+    const int bi = x / a.nl;
+    const size_t s_row = (((size_t)bi * a.nl_in + a.lrel0 + li) * a.kvh + h) * a.nrows + i;
     const size_t u = (size_t)a.u0 + ((size_t)li * a.batch + bi) * a.kvh + h;
     int pos = a.pos + i;
     if (pos >= a.rcap) pos -= a.rcap;
-    ring[(u * a.rcap + pos) * words_per_row + wd] = src[s_off];
+    ring[(u * a.rcap + pos) * words_per_row + wd] = src[s_row * words_per_row + wd];
   }
 }
 
@@ -72,12 +72,17 @@ __global__ void k_ring_copy(uint8_t *ring, uint8_t *dense, int e, int head, int 
 }  // namespace
 
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s) {
-  const int eb = kv_bf16 ? 2 : 4;
-  const size_t total = (size_t)a.batch * a.nl * a.kvh * a.nrows * (D * eb / 4);
-  size_t blocks = (total + NT - 1) / NT;
+  const int row_bytes = D * (kv_bf16 ? 2 : 4);
+  const int rows = a.batch * a.nl * a.kvh * a.nrows;
+  if (rows <= 0) return hipSuccess;
+  const bool wide = (((uintptr_t)a.src[0] | (uintptr_t)a.src[1]) & 15) == 0;
+  const int wpr = row_bytes / (wide ? 16 : 4);
+  size_t blocks = ((size_t)rows * wpr + NT - 1) / NT;
   if (blocks > 4096) blocks = 4096;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_ingest, dim3((unsigned)blocks, 2), dim3(NT), 0, s, a, eb);
+  if (wide)
+    hipLaunchKernelGGL(k_ingest<uint4>, dim3((unsigned)blocks, 2), dim3(NT), 0, s, a, wpr);
+  else
+    hipLaunchKernelGGL(k_ingest<uint32_t>, dim3((unsigned)blocks, 2), dim3(NT), 0, s, a, wpr);
   return hipGetLastError();
 }
 
