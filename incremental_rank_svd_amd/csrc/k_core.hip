@@ -113,16 +113,29 @@ __device__ __forceinline__ float quad_sum(float v) {
 // owner of column j+1 builds reflector j+1 as soon as it has applied
 // reflector j (one barrier per reflector). ld should be 4 mod 32 so that the
 // columns of different quads start in different banks.
-template <int RQ>
+template <int RQ, bool FULL>
 __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols, int nref, float *tau) {
+  // FULL: nrows == 4 RQ, so every row q + 4e exists. Then every load and
+  // store is unconditional (masking is arithmetic: v is zero above the
+  // diagonal, rows above it are written back unchanged), which lets a lane
+  // issue all RQ loads of a column back to back instead of one per branch.
   const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  auto inrange = [&](int row) { return FULL || row < nrows; };
   auto reflector = [&](int j) {
     float *cj = A + (size_t)j * ld;
     float s = 0.f;
+    float x[RQ];
 #pragma unroll
     for (int e = 0; e < RQ; e++) {
       const int row = q + 4 * e;
-      if (row > j && row < nrows) s += cj[row] * cj[row];
+      x[e] = 0.f;
+      if (FULL) {
+        x[e] = cj[row];
+      } else if (row < nrows) {
+        x[e] = cj[row];
+      }
+      const float t = (row > j && inrange(row)) ? x[e] : 0.f;
+      s += t * t;
     }
     s = quad_sum(s);
     const float x0 = cj[j];
@@ -135,9 +148,13 @@ __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols,
 #pragma unroll
     for (int e = 0; e < RQ; e++) {
       const int row = q + 4 * e;
-      if (row > j && row < nrows) cj[row] *= scal;
+      if (FULL) {
+        cj[row] = (row > j) ? x[e] * scal : ((row == j) ? beta : x[e]);
+      } else {
+        if (row > j && row < nrows) cj[row] = x[e] * scal;
+        if (row == j) cj[j] = beta;
+      }
     }
-    if ((j & 3) == q) cj[j] = beta;
     if (q == 0) tau[j] = tj;
   };
   if (nref > 0 && qid == 0) reflector(0);
@@ -150,29 +167,127 @@ __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols,
 #pragma unroll
       for (int e = 0; e < RQ; e++) {
         const int row = q + 4 * e;
-        v[e] = (row < nrows && row >= j) ? ((row == j) ? 1.f : cj[row]) : 0.f;
+        if (FULL) {
+          const float cv = cj[row];
+          v[e] = (row > j) ? cv : ((row == j) ? 1.f : 0.f);
+        } else {
+          v[e] = (row < nrows && row >= j) ? ((row == j) ? 1.f : cj[row]) : 0.f;
+        }
       }
       int col = qid;
       while (col <= j) col += NT / 4;
       for (; col < ncols; col += NT / 4) {
-        // two passes over the column (dot, then update): only v stays in registers
         float *cc = A + (size_t)col * ld;
-        float w = 0.f;
+        if (FULL) {
+          // column in registers: one pass of loads, one of stores
+          float x[RQ];
+          float w = 0.f;
 #pragma unroll
-        for (int e = 0; e < RQ; e++) {
-          const int row = q + 4 * e;
-          if (row < nrows && row >= j) w += v[e] * cc[row];
-        }
-        w = tj * quad_sum(w);
+          for (int e = 0; e < RQ; e++) {
+            x[e] = cc[q + 4 * e];
+            w += v[e] * x[e];
+          }
+          w = tj * quad_sum(w);
 #pragma unroll
-        for (int e = 0; e < RQ; e++) {
-          const int row = q + 4 * e;
-          if (row < nrows && row >= j) cc[row] -= w * v[e];
+          for (int e = 0; e < RQ; e++) cc[q + 4 * e] = x[e] - w * v[e];
+        } else {
+          // two passes over the column (dot, then update): only v stays in registers
+          float w = 0.f;
+#pragma unroll
+          for (int e = 0; e < RQ; e++) {
+            const int row = q + 4 * e;
+            if (row < nrows && row >= j) w += v[e] * cc[row];
+          }
+          w = tj * quad_sum(w);
+#pragma unroll
+          for (int e = 0; e < RQ; e++) {
+            const int row = q + 4 * e;
+            if (row < nrows && row >= j) cc[row] -= w * v[e];
+          }
         }
       }
     }
     if (j + 1 < nref && qid == ((j + 1) & (NT / 4 - 1))) reflector(j + 1);
     __syncthreads();
+  }
+}
+
+// Cyclic sweeps of one-sided Jacobi over the columns of J (c columns, column
+// stride sj, rows split over the 4 lanes of a quad, NQ float4 chunks per
+// lane), accumulating the same rotations in H. A quad owns one pair of the
+// parallel round-robin order per round; cosines are measured from fp64 dot
+// products. Stops after a sweep without rotation or at SWEEP_CAP.
+template <int NQ>
+__device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl, int c, int c2, double tol,
+                                              double negl, int &sweep, bool &conv) {
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  while (!conv && sweep < SWEEP_CAP) {
+    sweep++;
+    int rot = 0;
+    for (int rnd = 0; rnd < c2 - 1; rnd++) {
+      if (qid < c2 / 2) {
+        int ci, cj;
+        rr_pair(rnd, qid, c2, ci, cj);
+        if (cj < c) {
+          float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
+          float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
+          float4 xi[NQ], xj[NQ];
+          double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll
+          for (int e = 0; e < NQ; e++) {
+            xi[e] = zi[e];
+            xj[e] = zj[e];
+          }
+#pragma unroll
+          for (int e = 0; e < NQ; e++) {
+            const double a0 = xi[e].x, a1 = xi[e].y, a2 = xi[e].z, a3 = xi[e].w;
+            const double b0 = xj[e].x, b1 = xj[e].y, b2 = xj[e].z, b3 = xj[e].w;
+            al += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
+            be += b0 * b0 + b1 * b1 + b2 * b2 + b3 * b3;
+            ga += a0 * b0 + a1 * b1 + a2 * b2 + a3 * b3;
+          }
+          al = quad_sum_d(al);
+          be = quad_sum_d(be);
+          ga = quad_sum_d(ga);
+          if (al > negl && be > negl && fabs(ga) > tol * sqrt(al * be)) {
+            const double zeta = (be - al) / (2.0 * ga);
+            const double az = fabs(zeta);
+            double td = (az > 1e150) ? 0.5 / az : 1.0 / (az + sqrt(1.0 + az * az));
+            td = copysign(td, zeta);
+            const double csd = 1.0 / sqrt(1.0 + td * td);
+            const float cs = (float)csd;
+            const float sn = (float)(csd * td);
+            float4 *hi = (float4 *)(H + (size_t)ci * sj + q * rl);
+            float4 *hj = (float4 *)(H + (size_t)cj * sj + q * rl);
+            float4 yi[NQ], yj[NQ];
+#pragma unroll
+            for (int e = 0; e < NQ; e++) {
+              yi[e] = hi[e];
+              yj[e] = hj[e];
+            }
+#pragma unroll
+            for (int e = 0; e < NQ; e++) {
+              const float4 u0 = xi[e], u1 = xj[e];
+              zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                             cs * u0.w - sn * u1.w};
+              zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                             sn * u0.w + cs * u1.w};
+            }
+#pragma unroll
+            for (int e = 0; e < NQ; e++) {
+              const float4 u0 = yi[e], u1 = yj[e];
+              hi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                             cs * u0.w - sn * u1.w};
+              hj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                             sn * u0.w + cs * u1.w};
+            }
+            rot = 1;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    conv = !__syncthreads_or(rot);
   }
 }
 
@@ -268,7 +383,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
 
   if (p > 0) {
     // Householder QR of [B | E^T] (column j = LDS row j), c reflectors.
-    house_qr<D / 4>(A, LDA, D, k + b, c, tau);
+    house_qr<D / 4, true>(A, LDA, D, k + b, c, tau);
     // P = Q[:, k:k+p] = H_0 ... H_{c-1} [e_k .. e_{k+p-1}], accumulated backwards
     // in the registers of one quad per column (lane q: rows q, q+4, ...);
     // reflectors j > k+col leave e_{k+col} unchanged and are skipped.
@@ -280,18 +395,20 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
         const float tj = tau[j];
         if (tj == 0.f) continue;
         const float *cj = A + (size_t)j * LDA;
+        // reflector j as coefficients (v = 1 at row j, stored below it); all
+        // D rows are loaded unconditionally and masked arithmetically
+        float vj[D / 4];
         float w = 0.f;
 #pragma unroll
         for (int e = 0; e < D / 4; e++) {
           const int row = q + 4 * e;
-          w += (row > j) ? cj[row] * x[e] : ((row == j) ? x[e] : 0.f);
+          const float cv = cj[row];
+          vj[e] = (row > j) ? cv : ((row == j) ? 1.f : 0.f);
+          w += vj[e] * x[e];
         }
         w = tj * quad_sum(w);
 #pragma unroll
-        for (int e = 0; e < D / 4; e++) {
-          const int row = q + 4 * e;
-          x[e] -= (row > j) ? w * cj[row] : ((row == j) ? w : 0.f);
-        }
+        for (int e = 0; e < D / 4; e++) x[e] -= w * vj[e];
       }
 #pragma unroll
       for (int e = 0; e < D / 4; e++) Pg[(size_t)col * D + q + 4 * e] = x[e];
@@ -334,7 +451,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
       Zb[(size_t)col * mz + row] = v;
     }
     __syncthreads();
-    house_qr<2 * D / 4>(Zb, mz, m, c, c, tau);
+    house_qr<2 * D / 4, false>(Zb, mz, m, c, c, tau);
     // Move R (upper triangle, c x c) into the J layout through registers:
     // the packed upper triangle is dealt evenly over the threads, then the
     // (overlapping) J region is cleared and written.
@@ -389,73 +506,19 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     const double negl = (double)(ntol * ntol * fro2);
     __syncthreads();  // sv is reused below
     const int c2 = c + (c & 1);
-    const int nq4 = rl / 4;  // float4 chunks per quad lane
     int sweep = 0;
     bool conv = (c < 2);
-    while (!conv && sweep < SWEEP_CAP) {
-      sweep++;
-      int rot = 0;
-      for (int rnd = 0; rnd < c2 - 1; rnd++) {
-        if (qid < c2 / 2) {
-          int ci, cj;
-          rr_pair(rnd, qid, c2, ci, cj);
-          if (cj < c) {
-            float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
-            float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
-            float4 xi[D / 16], xj[D / 16];
-            double al = 0.0, be = 0.0, ga = 0.0;
-#pragma unroll
-            for (int e = 0; e < D / 16; e++) {
-              if (e < nq4) {
-                xi[e] = zi[e];
-                xj[e] = zj[e];
-                const double a0 = xi[e].x, a1 = xi[e].y, a2 = xi[e].z, a3 = xi[e].w;
-                const double b0 = xj[e].x, b1 = xj[e].y, b2 = xj[e].z, b3 = xj[e].w;
-                al += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
-                be += b0 * b0 + b1 * b1 + b2 * b2 + b3 * b3;
-                ga += a0 * b0 + a1 * b1 + a2 * b2 + a3 * b3;
-              }
-            }
-            al = quad_sum_d(al);
-            be = quad_sum_d(be);
-            ga = quad_sum_d(ga);
-            if (al > negl && be > negl && fabs(ga) > tol * sqrt(al * be)) {
-              const double zeta = (be - al) / (2.0 * ga);
-              const double az = fabs(zeta);
-              double td = (az > 1e150) ? 0.5 / az : 1.0 / (az + sqrt(1.0 + az * az));
-              td = copysign(td, zeta);
-              const double csd = 1.0 / sqrt(1.0 + td * td);
-              const float cs = (float)csd;
-              const float sn = (float)(csd * td);
-#pragma unroll
-              for (int e = 0; e < D / 16; e++) {
-                if (e < nq4) {
-                  const float4 u0 = xi[e], u1 = xj[e];
-                  zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
-                                 cs * u0.w - sn * u1.w};
-                  zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
-                                 sn * u0.w + cs * u1.w};
-                }
-              }
-              float4 *hi = (float4 *)(H + (size_t)ci * sj + q * rl);
-              float4 *hj = (float4 *)(H + (size_t)cj * sj + q * rl);
-#pragma unroll
-              for (int e = 0; e < D / 16; e++) {
-                if (e < nq4) {
-                  const float4 u0 = hi[e], u1 = hj[e];
-                  hi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
-                                 cs * u0.w - sn * u1.w};
-                  hj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
-                                 sn * u0.w + cs * u1.w};
-                }
-              }
-              rot = 1;
-            }
-          }
-        }
-        __syncthreads();
-      }
-      conv = !__syncthreads_or(rot);
+    // rows per quad lane as a compile-time constant: the loads of a column
+    // are then issued back to back
+    switch (rl / 4) {
+      case 1: jacobi_sweeps<1>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 2: jacobi_sweeps<2>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 3: jacobi_sweeps<3>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 4: jacobi_sweeps<4>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 5: jacobi_sweeps<5>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 6: jacobi_sweeps<6>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 7: jacobi_sweeps<7>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      default: jacobi_sweeps<8>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
     }
     if (tid == 0) {
       if (!conv) atomicOr(a.status, FLAG_SWEEP_CAP);
@@ -600,6 +663,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     const int i = e / kplus, j = e - i * kplus;
     const float *bi = Bp + (size_t)i * D, *bj = Bp + (size_t)j * D;
     double acc = 0.0;
+#pragma unroll 2
     for (int t = 0; t < D / 4; t++) {
       const int v = 4 * ((t + i + j) & (D / 4 - 1));  // rotate the start: fewer bank conflicts
       const float4 x = *reinterpret_cast<const float4 *>(bi + v);
@@ -720,7 +784,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
 }
 
 template <int NR, typename TK, typename TC>
-__global__ void __launch_bounds__(NT, 2) k_core(const FoldArgs a) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) k_core(const FoldArgs a) {
   extern __shared__ float smem[];
   if (blockIdx.y == 0)
     core_body<NR, TK, TC, 0>(a, smem);
