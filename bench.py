@@ -37,7 +37,24 @@ def parse():
     p.add_argument("--sample-every", type=int, default=16, help="event-time every n-th decode launch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (default: one per core, <= 32)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 1 GiB device-to-device copy and exit (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """One plain copy kernel of known size: 1 GiB read, 1 GiB written. Under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its counter readings give the
+    factor that turns those counters into bytes."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)  # an elementwise kernel: 1 GiB in, 1 GiB out
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
 def decode_bytes(U, g, n, e, kK, kV, coord_b, kv_b):
@@ -96,6 +113,9 @@ def cpu_baseline(w, nunits):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the compressed-cache path has no cross-GPU step "
               "(units are independent); run with --gpus 1", file=sys.stderr)
