@@ -4,8 +4,9 @@ One step = one whole decode run of the workload on synthetic inputs already
 resident in HBM: starting from an empty cache, every token appends one K and
 one V row to every layer (the window's oldest 64 rows fold into the low-rank
 history whenever it holds w + b rows) and then runs decode attention over the
-compressed cache of every layer. For the Llama-3-8B-shaped workload that is
-8192 tokens x 32 layers x 8 kv heads, 126 fold rounds per unit stream.
+compressed cache of every layer, both through one iskv_append_decode call per
+token. For the Llama-3-8B-shaped workload that is 8192 tokens x 32 layers x
+8 kv heads, 126 fold rounds per unit stream.
 
 Printed: one JSON line (metric, value = KV rows folded into history per
 second over the whole job, roofline of the dominant kernel measured with HIP
@@ -57,12 +58,13 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
-def decode_bytes(U, g, n, e, kK, kV, coord_b, kv_b):
+def decode_bytes(U, g, n, e, kK, kV, coord_b, kv_b, appended=0):
     """Algorithmic HBM bytes of one decode launch over U units: history
-    coordinates of K and V, window rows of K and V, both bases, queries in,
-    outputs out (fp32)."""
+    coordinates of K and V, window rows of K and V (e includes an appended
+    row, read from the caller's buffer), both bases, queries in, outputs out
+    (fp32), and the appended K and V rows written to the window ring."""
     per = (n * (kK + kV) * coord_b + 2 * e * 128 * kv_b + (kK + kV) * 128 * 4
-           + g * 128 * kv_b + g * 128 * 4)
+           + g * 128 * kv_b + g * 128 * 4 + appended * 2 * 128 * kv_b)
     return U * per
 
 
@@ -159,7 +161,7 @@ def main():
     kstr = K[0].numel() * K.element_size()
     qstr = Q[0].numel() * Q.element_size()
     scale = ctypes.c_float(128 ** -0.5)
-    append, decode = lib.iskv_append_block, lib.iskv_decode_attn
+    step_call, decode = lib.iskv_append_decode, lib.iskv_decode_attn
     VP = ctypes.c_void_p
     n_sample = max(1, args.sample_every)
 
@@ -170,28 +172,27 @@ def main():
         b, wnd = w.block, w.window
         ev = []
         for t in range(T):
-            rc = append(h, VP(kp0 + t * kstr), VP(vp0 + t * kstr), 1, 0, L, sp)
-            if rc:
-                raise RuntimeError("append failed: %d" % rc)
             e += 1
-            if e >= wnd + b:  # a fold ran inside this append
+            folds = e >= wnd + b  # this token's append folds: the call runs ingest, fold, decode
+            if folds:
                 p = min(b, 128 - kK)
                 kK = min(w.rank_k, kK + p)
                 p = min(b, 128 - kV)
                 kV = min(w.rank_v, kV + p)
                 n += b
                 e -= b
-            if sampled is not None and t % n_sample == 0:
+            args = (h, VP(kp0 + t * kstr), VP(vp0 + t * kstr), VP(qp0 + t * qstr), op, 0, L, scale, sp)
+            if sampled is not None and not folds and t % n_sample == 0:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                rc = decode(h, VP(qp0 + t * qstr), op, 0, L, scale, sp)
+                rc = step_call(*args)
                 e1.record(stream)
-                ev.append((e0, e1, decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b)))
+                ev.append((e0, e1, decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, appended=1)))
             else:
-                rc = decode(h, VP(qp0 + t * qstr), op, 0, L, scale, sp)
+                rc = step_call(*args)
             if rc:
-                raise RuntimeError("decode failed: %d" % rc)
+                raise RuntimeError("append_decode failed: %d" % rc)
         if sampled is not None:
             sampled.extend(ev)
         return n

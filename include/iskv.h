@@ -120,6 +120,20 @@ ISKV_API int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows
 ISKV_API int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers,
                      float scale, void *stream);
 
+/* One decode step in one call: append one new K and V row per sequence and
+ * kv head (as iskv_append_block with nrows = 1), then decode attention over
+ * the updated cache (as iskv_decode_attn), for layers layer0..layer0+nlayers-1.
+ * k_rows, v_rows: [batch][nlayers][kv_heads][1][d]; q, out as in
+ * iskv_decode_attn. Results are those of the two calls in sequence. When the
+ * append does not fold and the bf16 matrix-core decode applies (bf16
+ * coordinates and rows, ranks multiples of 8, 16-byte aligned q and rows,
+ * window in LDS), a single launch copies the new rows into the window ring
+ * and attends over them; otherwise the two calls run. Errors: as the two
+ * calls; argument and capacity errors leave the state unchanged. Sections
+ * "Block-Incremental Decoding Updates" and "Reconstruction and Storage". */
+ISKV_API int iskv_append_decode(iskv_t h, const void *k_rows, const void *v_rows, const void *q, float *out,
+                                int32_t layer0, int32_t nlayers, float scale, void *stream);
+
 /* Reconstruction of one unit (section "Reconstruction and Storage"):
  * dev_out [(n+e) x d] fp32 = history rows C B^T, then the window rows
  * oldest first. which: 0 = K, 1 = V. */

@@ -297,6 +297,27 @@ int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t
   return ISKV_OK;
 }
 
+static DecodeArgs decode_args(iskv_t h, const void *q, float *out, int layer0, int nlayers, int l0, int l1,
+                              float scale) {
+  DecodeArgs a = {};
+  a.L = h->L;
+  a.q = q;
+  a.out = out;
+  a.nl_in = nlayers;
+  a.lrel0 = l0 - layer0;
+  a.nl = l1 - l0;
+  a.u0 = l0 * h->L.batch * h->L.kvh;
+  a.n = h->n[l0];
+  a.e = h->e[l0];
+  a.kK = h->kk[l0];
+  a.kV = h->kv[l0];
+  a.head = h->head[l0];
+  const int chunk = decode_chunk_rows(h->L);
+  a.nchunk = (a.n + chunk - 1) / chunk;
+  a.scale = scale;
+  return a;
+}
+
 int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers, float scale,
                      void *stream) {
   if (!h || !q || !out) return ISKV_ERR_ARG;
@@ -307,24 +328,50 @@ int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_
   hipStream_t s = (hipStream_t)stream;
   for (int l0 = layer0; l0 < layer0 + nlayers;) {
     const int l1 = run_end(h, l0, layer0 + nlayers);
-    DecodeArgs a = {};
-    a.L = h->L;
-    a.q = q;
-    a.out = out;
-    a.nl_in = nlayers;
-    a.lrel0 = l0 - layer0;
-    a.nl = l1 - l0;
-    a.u0 = l0 * h->L.batch * h->L.kvh;
-    a.n = h->n[l0];
-    a.e = h->e[l0];
-    a.kK = h->kk[l0];
-    a.kV = h->kv[l0];
-    a.head = h->head[l0];
-    const int chunk = decode_chunk_rows(h->L);
-    a.nchunk = (a.n + chunk - 1) / chunk;
-    a.scale = scale;
+    const DecodeArgs a = decode_args(h, q, out, layer0, nlayers, l0, l1, scale);
     int rc = fail_hip(h, launch_decode(a, s));
     if (rc) return rc;
+    l0 = l1;
+  }
+  return ISKV_OK;
+}
+
+int iskv_append_decode(iskv_t h, const void *k_rows, const void *v_rows, const void *q, float *out,
+                       int32_t layer0, int32_t nlayers, float scale, void *stream) {
+  if (!h || !k_rows || !v_rows || !q || !out) return ISKV_ERR_ARG;
+  if (h->poisoned) return ISKV_ERR_POISONED;
+  if (bad_layers(h, layer0, nlayers)) return ISKV_ERR_ARG;
+  const int w = h->L.w, b = h->L.b;
+  bool fuse = true;
+  for (int l = layer0; l < layer0 + nlayers; l++) {
+    const int e2 = h->e[l] + 1;
+    if ((long long)h->n[l] + e2 > h->cfg.max_tokens) return ISKV_ERR_CAPACITY;
+    if (e2 >= w + b && h->n[l] + b > h->L.ncap) return ISKV_ERR_CAPACITY;
+    if (e2 >= w + b) fuse = false;  // this append folds: ingest, fold, then decode
+  }
+  for (int l0 = layer0; fuse && l0 < layer0 + nlayers;) {
+    const int l1 = run_end(h, l0, layer0 + nlayers);
+    DecodeArgs a = decode_args(h, q, out, layer0, nlayers, l0, l1, scale);
+    a.nk = k_rows;
+    a.nv = v_rows;
+    fuse = decode_can_fuse(a);
+    l0 = l1;
+  }
+  if (!fuse) {
+    const int rc = iskv_append_block(h, k_rows, v_rows, 1, layer0, nlayers, stream);
+    if (rc) return rc;
+    return iskv_decode_attn(h, q, out, layer0, nlayers, scale, stream);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int l0 = layer0; l0 < layer0 + nlayers;) {
+    const int l1 = run_end(h, l0, layer0 + nlayers);
+    DecodeArgs a = decode_args(h, q, out, layer0, nlayers, l0, l1, scale);
+    a.nk = k_rows;
+    a.nv = v_rows;
+    a.nnew = 1;
+    const int rc = fail_hip(h, launch_decode(a, s));
+    if (rc) return rc;
+    for (int l = l0; l < l1; l++) h->e[l] += 1;
     l0 = l1;
   }
   return ISKV_OK;

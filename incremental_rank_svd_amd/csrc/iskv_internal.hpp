@@ -91,6 +91,10 @@ struct DecodeArgs {
   int nchunk;
   float scale;
   int wlds;  // window rows staged in LDS (set by the launcher)
+  // fused append: one new K and V row per unit ([batch][nl_in][kvh][1][D]),
+  // written to the ring at position e and attended as window row e
+  const void *nk, *nv;
+  int nnew;
 };
 
 // ---------------------------------------------------------------------------
@@ -153,6 +157,8 @@ hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf1
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);  // K and V
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+// true when launch_decode can take the appended row itself (nnew = 1)
+bool decode_can_fuse(const DecodeArgs &a);
 int decode_chunk_rows(const Layout &L);  // history rows per decode block
 hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, int e, int head,
                               float *out, hipStream_t s);

@@ -338,8 +338,11 @@ __host__ __device__ inline size_t decode_unit_big(int rsV, int g) {
                       (size_t)g * rsV + (size_t)g * D + 8 * MAXG;
   return tiles > comb ? tiles : comb;
 }
+// staged window rows are padded to WSTR bf16 (272 bytes): 16 lanes reading 16
+// consecutive rows then fall into distinct banks
+constexpr int WSTR = D + 8;
 __host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV, int g, int ewin) {
-  return sizeof(float) * (decode_unit_qs(rsK) + decode_unit_big(rsV, g) + (size_t)ewin * D);
+  return sizeof(float) * (decode_unit_qs(rsK) + decode_unit_big(rsV, g) + (size_t)ewin * WSTR);
 }
 
 // Window rows of the workgroup's window share: from the LDS copy or the ring.
@@ -480,10 +483,9 @@ __device__ __forceinline__ void window_part(const DecodeArgs &a, const uint16_t 
 // bf16, the scale applied to the fp32 scores) and 128 value columns (8 tiles).
 // Wave wv takes the 32-row steps wv, wv + NWU, ...; every wave leaves its
 // (max, sum, values) per head in wo[wv].
-__device__ __forceinline__ void window_mfma(const DecodeArgs &a, const u32x4_t *qfrag, const uint16_t *wk,
+__device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u32x4_t *qfrag, const uint16_t *wk,
                                             const uint16_t *wvr, float *wo, int g, int wv, int lane) {
   const int hq = lane & 15, qd = lane >> 4;
-  const int e = a.e;
   float m = -INFINITY, l = 0.f;
   f32x4_t acc[8];
 #pragma unroll
@@ -495,8 +497,8 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, const u32x4_t *
     for (int kc = 0; kc < 4; kc++) {
       const int col = kc * 32 + 8 * qd;
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      const u32x4_t k0 = (r0 < e) ? *(const u32x4_t *)(wk + (size_t)r0 * D + col) : z;
-      const u32x4_t k1 = (r1 < e) ? *(const u32x4_t *)(wk + (size_t)r1 * D + col) : z;
+      const u32x4_t k0 = (r0 < e) ? *(const u32x4_t *)(wk + (size_t)r0 * WSTR + col) : z;
+      const u32x4_t k1 = (r1 < e) ? *(const u32x4_t *)(wk + (size_t)r1 * WSTR + col) : z;
       const u32x4_t bq = qfrag[kc * 64 + lane];
       d0 = mfma16(k0, bq, d0);
       d1 = mfma16(k1, bq, d1);
@@ -533,7 +535,7 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, const u32x4_t *
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const int row = rb + ((i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4));
-        v8[i] = (row < e) ? wvr[(size_t)row * D + col] : (uint16_t)0;
+        v8[i] = (row < e) ? wvr[(size_t)row * WSTR + col] : (uint16_t)0;
       }
       const u32x4_t av = {pack2(v8[0], v8[1]), pack2(v8[2], v8[3]), pack2(v8[4], v8[5]), pack2(v8[6], v8[7])};
       acc[nt] = mfma16(av, phi, acc[nt]);
@@ -565,7 +567,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);    // [(kc*2 + part)*64 + lane]
   u32x4_t *qfrag = frag + 4 * 2 * 64;                        // [kc*64 + lane]: q itself (bf16)
   float *big = qsm + decode_unit_qs(rsK);                   // tiles, then combine scratch
-  uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g));  // [2][e][D] window copy
+  uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g));  // [2][e][WSTR] window copy
   int li, bi, h;
   unit_coords(a, ul, li, bi, h);
   const uint16_t *q = (const uint16_t *)a.q + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
@@ -574,7 +576,9 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   // The window rows are copied to LDS in batches of WB 16-byte chunks per
   // thread; the first batch's loads are in flight during the q' projection.
   constexpr int WB = 8;
-  const int wch = a.wlds ? 2 * a.e * (D / 8) : 0;  // K rows, then V rows
+  const int ew = a.e + a.nnew;                      // window rows, the appended one last
+  const int wch = a.wlds ? 2 * ew * (D / 8) : 0;  // K rows, then V rows
+  const size_t nrow_off = (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.kvh + h) * D;
   u32x4_t wbuf[WB];
   auto win_load = [&](int c0) {
 #pragma unroll
@@ -582,10 +586,12 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       const int c = c0 + z * NTU + tid;
       wbuf[z] = u32x4_t{0u, 0u, 0u, 0u};
       if (c < wch) {
-        const int which = c >= a.e * (D / 8);
-        const int rem = c - which * a.e * (D / 8);
+        const int which = c >= ew * (D / 8);
+        const int rem = c - which * ew * (D / 8);
         const int i = rem >> 4, part = rem & 15;
-        wbuf[z] = *(const u32x4_t *)(win_row<false>(which ? vr : kr, i, a.head, a.L.rcap) + part * 8);
+        const uint16_t *src = (i < a.e) ? win_row<false>(which ? vr : kr, i, a.head, a.L.rcap)
+                                        : (const uint16_t *)(which ? a.nv : a.nk) + nrow_off;
+        wbuf[z] = *(const u32x4_t *)(src + part * 8);
       }
     }
   };
@@ -593,7 +599,16 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
 #pragma unroll
     for (int z = 0; z < WB; z++) {
       const int c = c0 + z * NTU + tid;
-      if (c < wch) *(u32x4_t *)(wsm + (size_t)c * 8) = wbuf[z];
+      if (c < wch) {
+        const int which = c >= ew * (D / 8);
+        const int rem = c - which * ew * (D / 8);
+        const int i = rem >> 4, part = rem & 15;
+        *(u32x4_t *)(wsm + ((size_t)which * ew + i) * WSTR + part * 8) = wbuf[z];
+        if (i >= a.e) {  // the appended row also enters the ring
+          uint16_t *ring = (uint16_t *)(which ? a.L.X[1].ring : a.L.X[0].ring) + (size_t)u * a.L.rcap * D;
+          *(u32x4_t *)((uint16_t *)win_row<false>(ring, i, a.head, a.L.rcap) + part * 8) = wbuf[z];
+        }
+      }
     }
   };
   if (wch > 0) win_load(0);
@@ -741,6 +756,21 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     }
   }
   __syncthreads();  // tiles are free from here on
+  // B_V for the output projection, loaded now so that the window and combine
+  // phases hide the latency: output element (hh, t) is split over jsplit
+  // adjacent lanes, lane part jp holding B_V[j][t] for j = jp, jp + jsplit, ...
+  const int jsplit = (g * D >= NTU) ? 1 : NTU / (g * D);  // 1, 2, 4 or 8
+  const bool bv_early = rsV <= 16 * jsplit && g * D <= NTU;
+  const int ot = tid / jsplit, jp = tid - ot * jsplit;
+  const float *Bv = a.L.X[1].Bt + (size_t)u * rsV * D;
+  float bvr[16];
+  if (bv_early) {
+#pragma unroll
+    for (int z = 0; z < 16; z++) {
+      const int j = jp + jsplit * z;
+      bvr[z] = (ot < g * D && j < a.kV) ? Bv[(size_t)j * D + (ot & (D - 1))] : 0.f;
+    }
+  }
   float *hm = big;                                  // [NWU][MAXG] max
   float *hl = hm + NWU * MAXG;                      // [NWU][MAXG] sum
   float *ha = hl + NWU * MAXG;                      // [NWU][g][rsV] o'
@@ -763,7 +793,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   }
   // ---- window rows: row i goes to lane group (i mod 64) of the workgroup ----
   if (a.wlds)
-    window_mfma(a, qfrag, wsm, wsm + (size_t)a.e * D, wo, g, wv, lane);
+    window_mfma(a, ew, qfrag, wsm, wsm + (size_t)ew * WSTR, wo, g, wv, lane);
   else
     window_part(a, q, kr, vr, wo, g, wv, lane);
   __syncthreads();
@@ -803,13 +833,26 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     ow[idx] = s;
   }
   __syncthreads();
-  const float *Bv = a.L.X[1].Bt + (size_t)u * rsV * D;
   float *out = (float *)a.out + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
-  for (int idx = tid; idx < g * D; idx += NTU) {
-    const int hh = idx / D, t = idx - hh * D;
-    float s = ow[idx];
-    for (int j = 0; j < a.kV; j++) s += op[hh * rsV + j] * Bv[(size_t)j * D + t];
-    out[idx] = s / fac[hh * 8 + 1];
+  if (bv_early) {
+    const int hh = ot / D;
+    float s = 0.f;
+    if (ot < g * D) {
+#pragma unroll
+      for (int z = 0; z < 16; z++) {
+        const int j = jp + jsplit * z;
+        if (j < rsV) s += op[hh * rsV + j] * bvr[z];
+      }
+    }
+    for (int off = 1; off < jsplit; off <<= 1) s += __shfl_xor(s, off);
+    if (ot < g * D && jp == 0) out[ot] = (ow[ot] + s) / fac[hh * 8 + 1];
+  } else {
+    for (int idx = tid; idx < g * D; idx += NTU) {
+      const int hh = idx / D, t = idx - hh * D;
+      float s = ow[idx];
+      for (int j = 0; j < a.kV; j++) s += op[hh * rsV + j] * Bv[(size_t)j * D + t];
+      out[idx] = s / fac[hh * 8 + 1];
+    }
   }
 }
 
@@ -817,8 +860,9 @@ template <int KS, int NTV>
 hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
   DecodeArgs a = a0;
   // stage the window in LDS when it fits next to the rest (160 KB per workgroup)
-  size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, a.e);
-  a.wlds = (a.e > 0 && lds <= 160 * 1024 && ((uintptr_t)a.q & 15) == 0) ? 1 : 0;
+  const int ew = a.e + a.nnew;
+  size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, ew);
+  a.wlds = (ew > 0 && lds <= 160 * 1024 && ((uintptr_t)a.q & 15) == 0) ? 1 : 0;
   if (!a.wlds) lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, 0);
   hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -854,6 +898,12 @@ hipError_t launch_decode_t(const DecodeArgs &a, int nunits, hipStream_t s) {
 }  // namespace
 
 int decode_chunk_rows(const Layout &L) { return L.chunk; }
+
+bool decode_can_fuse(const DecodeArgs &a) {
+  if (!(a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0)) return false;
+  if ((((uintptr_t)a.q | (uintptr_t)a.nk | (uintptr_t)a.nv) & 15) != 0) return false;
+  return decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, a.e + 1) <= 160 * 1024;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   const int nunits = a.L.batch * a.nl * a.L.kvh;

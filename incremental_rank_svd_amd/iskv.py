@@ -32,7 +32,7 @@ FLAG_NONFINITE = 0x2
 
 EXPORTED = [
     "iskv_workspace_bytes", "iskv_init", "iskv_reset", "iskv_append_block", "iskv_prefill_block",
-    "iskv_decode_attn", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
+    "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
 ]
 
@@ -70,6 +70,7 @@ def load(path: str = None):
     lib.iskv_append_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.iskv_prefill_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
     lib.iskv_decode_attn.argtypes = [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
+    lib.iskv_append_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
     lib.iskv_reconstruct.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
     P32 = ctypes.POINTER(_i32)
     lib.iskv_counts.argtypes = [_vp, _i32, P32, P32, P32, P32]
@@ -193,6 +194,24 @@ class Cache:
         s = float(c.head_dim ** -0.5) if scale is None else float(scale)
         _check(self.lib.iskv_decode_attn(self.h, qp, op, layer0, nl, ctypes.c_float(s), _stream(stream)),
                "iskv_decode_attn")
+        return out
+
+    def append_decode(self, k_rows, v_rows, q, out=None, layer0=0, scale=None, stream=None):
+        """One decode step: k_rows, v_rows [batch, nlayers, kv_heads, 1, 128] and
+        q [batch, nlayers, q_heads, 128] in kv dtype; returns fp32 out like q."""
+        c = self.cfg
+        nl = q.shape[1]
+        rshape = (c.batch, nl, c.kv_heads, 1, c.head_dim)
+        qshape = (c.batch, nl, c.q_heads, c.head_dim)
+        if out is None:
+            out = torch.empty(qshape, dtype=torch.float32, device=self.device)
+        kp = self._t(k_rows, rshape, self.kv_dtype, "k_rows")
+        vp = self._t(v_rows, rshape, self.kv_dtype, "v_rows")
+        qp = self._t(q, qshape, self.kv_dtype, "q")
+        op = self._t(out, qshape, torch.float32, "out")
+        s = float(c.head_dim ** -0.5) if scale is None else float(scale)
+        _check(self.lib.iskv_append_decode(self.h, kp, vp, qp, op, layer0, nl, ctypes.c_float(s),
+                                           _stream(stream)), "iskv_append_decode")
         return out
 
     def counts(self, layer=0):

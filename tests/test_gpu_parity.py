@@ -355,3 +355,49 @@ def test_bf16_decode_rank_and_group_shapes(iskv, rk, rv, g, b):
         derr = _check_decode(cache, w, q, out, [(0, 0, 0), (0, 0, 1)])
     assert cache.status() == 0
     note("  decode err %.2e" % derr)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(),                                                            # fused launch (bf16, window in LDS)
+    dict(block=128, rank_k=64, rank_v=96, window=256, decode_tokens=700),  # window too big for LDS: two calls
+    dict(coord_dtype="f32", decode_tokens=400),                        # fp32 coordinates: two calls
+])
+def test_append_decode_equals_append_then_decode(iskv, shape):
+    """iskv_append_decode gives bit-identical outputs and state to
+    iskv_append_block(nrows = 1) followed by iskv_decode_attn, across folds."""
+    from dataclasses import replace
+
+    base = dict(layers=2, kv_heads=4, q_heads=16, decode_tokens=450, cfg_id=31)
+    base.update(shape)
+    w = replace(synth.get_config(1), **base)
+    note("case: append_decode %s" % shape)
+    T = w.total_tokens
+    rows = _rows_all(w, T)
+    dt = tdtype(w.kv_dtype)
+    K = to_dev(rows["K"], dt, DEV)
+    V = to_dev(rows["V"], dt, DEV)
+    A = _cache(iskv, w, coord=w.coord_dtype)
+    B = _cache(iskv, w, coord=w.coord_dtype)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    worst = 0
+    for t in range(T):
+        q = torch.randn((w.batch, w.layers, w.q_heads, D), generator=gen, device=DEV).to(dt)
+        kt = K[:, :, :, t:t + 1].contiguous()
+        vt = V[:, :, :, t:t + 1].contiguous()
+        oa = A.append_decode(kt, vt, q)
+        B.append_block(kt, vt)
+        ob = B.decode_attn(q)
+        if t % 37 == 0 or t == T - 1:
+            assert A.counts(0) == B.counts(0)
+            d = (oa - ob).abs().max().item()
+            worst = max(worst, d)
+            assert d == 0.0, (t, d)
+    assert A.status() == 0 and B.status() == 0
+    for x in (0, 1):
+        for (l, h) in ((0, 0), (1, 3)):
+            sa = A.export_state(x, 0, l, h)
+            sb = B.export_state(x, 0, l, h)
+            for ta, tb in zip(sa, sb):
+                assert torch.equal(ta, tb)
+    note("  %d steps, max |out difference| %.1e, final counts %s" % (T, worst, A.counts(0)))
