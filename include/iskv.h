@@ -67,6 +67,14 @@ typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1 } iskv_dtype;
 #define ISKV_FLAG_SWEEP_CAP 0x1u /* a core SVD stopped at its sweep cap */
 #define ISKV_FLAG_NONFINITE 0x2u /* a core produced a non-finite singular value */
 
+/* Update modes. ISKV_MODE_JOINT is the method; the other two are the
+ * ablations the pages discuss, for measuring what the joint update buys
+ * (section "The Basis Drift Problem", section "Ablation Study"). */
+#define ISKV_MODE_JOINT 0        /* basis and every stored row's coordinates rotated together */
+#define ISKV_MODE_FIXED_COORDS 1 /* basis updated, stored rows keep their coordinates (drift) */
+#define ISKV_MODE_FIXED_BASIS 2  /* once a basis exists it is kept; new rows are stored as
+                                    their projections F B, rank and sigma stay */
+
 typedef struct {
   int32_t batch;       /* sequences, >= 1 */
   int32_t layers;      /* >= 1 */
@@ -95,6 +103,11 @@ ISKV_API int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, vo
 /* Forget all tokens (host counters only; state memory is overwritten as the
  * cache refills) and clear the numeric flags on `stream`. */
 ISKV_API int iskv_reset(iskv_t h, void *stream);
+
+/* Select the update mode used by later folds of every layer (one of the
+ * ISKV_MODE_* values; ISKV_ERR_ARG otherwise). Host state only; takes effect
+ * with the next fold. */
+ISKV_API int iskv_set_mode(iskv_t h, int32_t mode);
 
 /* Append `nrows` (1..b) new K and V rows per sequence and kv head to layers
  * layer0 .. layer0+nlayers-1. k_rows, v_rows: [batch][nlayers][kv_heads][nrows][d]

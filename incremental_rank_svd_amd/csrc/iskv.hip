@@ -19,7 +19,12 @@ struct iskv_ctx {
   size_t ws_bytes;
   std::vector<int> n, e, head, kk, kv;
   bool poisoned;
+  int mode;  // ISKV_MODE_*
 };
+
+static_assert(MODE_JOINT == ISKV_MODE_JOINT && MODE_FIXED_COORDS == ISKV_MODE_FIXED_COORDS &&
+                  MODE_FIXED_BASIS == ISKV_MODE_FIXED_BASIS,
+              "mode values");
 
 namespace {
 
@@ -158,9 +163,22 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
   a.bmax = L.b;
   a.pmax = scratch_rows(L.b, L.X[0].r, L.X[1].r);
   a.status = L.status;
+  a.mode = h->mode;
+  if (h->mode == ISKV_MODE_FIXED_BASIS && a.k[0] > 0 && a.k[1] > 0) {
+    // the basis exists and is kept: store the block's projections, no core
+    int rc = fail_hip(h, launch_project(a, nunits, L.kv_bf16, L.coord_bf16, s));
+    if (rc) return rc;
+    for (int l = l0; l < l1; l++) {
+      h->n[l] += L.b;
+      h->e[l] -= L.b;
+      h->head[l] = (h->head[l] + L.b) % L.rcap;
+    }
+    return ISKV_OK;
+  }
+  if (a.mode == ISKV_MODE_FIXED_BASIS) a.mode = ISKV_MODE_JOINT;  // first fold builds the basis
   int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
   if (rc) return rc;
-  if (n > 0) {
+  if (n > 0 && a.mode == ISKV_MODE_JOINT) {
     ra.u0 = u0;
     ra.n = n;
     ra.ncap = L.ncap;
@@ -233,6 +251,7 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *strea
   h->kk.assign(cfg->layers, 0);
   h->kv.assign(cfg->layers, 0);
   h->poisoned = false;
+  h->mode = ISKV_MODE_JOINT;
   if (launch_zero(dev_ws, need, (hipStream_t)stream) != hipSuccess) {
     delete h;
     return ISKV_ERR_HIP;
@@ -246,6 +265,14 @@ int iskv_reset(iskv_t h, void *stream) {
   if (h->poisoned) return ISKV_ERR_POISONED;
   for (int l = 0; l < h->L.layers; l++) h->n[l] = h->e[l] = h->head[l] = h->kk[l] = h->kv[l] = 0;
   return fail_hip(h, launch_zero(h->L.status, 64, (hipStream_t)stream));
+}
+
+int iskv_set_mode(iskv_t h, int32_t mode) {
+  if (!h) return ISKV_ERR_ARG;
+  if (mode != ISKV_MODE_JOINT && mode != ISKV_MODE_FIXED_COORDS && mode != ISKV_MODE_FIXED_BASIS)
+    return ISKV_ERR_ARG;
+  h->mode = mode;
+  return ISKV_OK;
 }
 
 int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows, int32_t layer0,

@@ -11,6 +11,8 @@ namespace iskv {
 
 constexpr int D = 128;         // head dimension
 constexpr int NT = 256;        // threads per workgroup (4 wavefronts)
+// update modes, same values as ISKV_MODE_* in iskv.h
+constexpr int MODE_JOINT = 0, MODE_FIXED_COORDS = 1, MODE_FIXED_BASIS = 2;
 constexpr int SWEEP_CAP = 40;  // core SVD sweep cap (flagged when reached)
 
 constexpr uint32_t FLAG_SWEEP_CAP = 0x1u;
@@ -67,6 +69,7 @@ struct FoldArgs {
   int pmax;          // rows of D floats per unit of the fold scratch (scratch_rows)
   uint32_t *status;
   int lds_small[2];  // float offset of the small arrays in dynamic LDS, per kind
+  int mode;          // ISKV_MODE_JOINT or ISKV_MODE_FIXED_COORDS (fixed basis: launch_project)
 };
 
 struct RewriteArgs {
@@ -156,6 +159,8 @@ size_t core_lds_bytes(int k, int b, int r);
 hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);  // grid (nunits, 2)
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);  // K and V
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
+// fixed-basis fold: new rows C[n + i] = F_i B (k columns), discarded energy
+hipError_t launch_project(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // true when launch_decode can take the appended row itself (nnew = 1)
 bool decode_can_fuse(const DecodeArgs &a);

@@ -558,10 +558,11 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     perm[rank] = tid;
   }
   __syncthreads();
+  const float sig_jac = (tid < kplus) ? sv[perm[tid]] : 0.f;  // the core's singular value, rank tid
   {
     float *sig_new = X.sig + (size_t)u * r;
     // the old sigma was read only in phase B; safe to overwrite now
-    if (tid < r) sig_new[tid] = (tid < kplus) ? sv[perm[tid]] : 0.f;
+    if (tid < r) sig_new[tid] = sig_jac;
     if (tid == 0) {
       float dsum = 0.f;
       for (int qq = kplus; qq < c; qq++) dsum += sv[perm[qq]] * sv[perm[qq]];
@@ -779,7 +780,12 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
       for (int l = 0; l < k; l++) s2 += (tau[l] * hc[l]) * (tau[l] * hc[l]);
       for (int g = 0; g < ngrp; g++) s2 += part[g * r + tid];
     }
-    X.sig[(size_t)u * r + tid] = sqrtf(s2);
+    // With fixed coordinates the stored old rows are not rotated, so their
+    // column norms mean nothing: sigma is the core's (times its correction).
+    if (a.mode == MODE_FIXED_COORDS)
+      X.sig[(size_t)u * r + tid] = (tid < kplus) ? sig_jac * (1.f + Gg[(size_t)tid * kplus + tid]) : 0.f;
+    else
+      X.sig[(size_t)u * r + tid] = sqrtf(s2);
   }
 }
 

@@ -32,6 +32,61 @@ __global__ void __launch_bounds__(NT) k_ingest(const IngestArgs a, int words_per
   }
 }
 
+// Fixed-basis fold ([iS-KV] Ablation Study, "keeping bases fixed"): the b
+// oldest window rows F are stored as their coordinates F B in the kept basis
+// (zero beyond the rank); rank, basis and sigma stay; the discarded energy is
+// ||F||^2 - ||F B||^2, the part of F outside the basis. F and B go through LDS.
+template <typename TK, typename TC, int XK>
+__device__ __forceinline__ void project_body(const FoldArgs &a, float *sm) {
+  const Stream &X = a.X[XK];
+  const int k = a.k[XK], r = a.r[XK], b = a.b;
+  const int u = a.u0 + blockIdx.x;
+  float *Bs = sm;                  // k x D
+  float *Fs = sm + (size_t)k * D;  // b x D
+  float *red = Fs + (size_t)b * D; // NT / 64 partial sums
+  const float *Bt = X.Bt + (size_t)u * r * D;
+  const TK *ring = (const TK *)X.ring + (size_t)u * a.rcap * D;
+  for (int idx = threadIdx.x; idx < k * D; idx += NT) Bs[idx] = Bt[idx];
+  for (int idx = threadIdx.x; idx < b * D; idx += NT) {
+    const int i = idx / D, t = idx - i * D;
+    int pos = a.head + i;
+    if (pos >= a.rcap) pos -= a.rcap;
+    Fs[idx] = ldf<TK>(ring, (size_t)pos * D + t);
+  }
+  __syncthreads();
+  TC *C = (TC *)X.C + ((size_t)u * a.ncap + a.n) * r;
+  float lost = 0.f;
+  for (int idx = threadIdx.x; idx < b * r; idx += NT) {
+    const int i = idx / r, j = idx - i * r;
+    float y = 0.f;
+    if (j < k) {
+      const float *f = Fs + (size_t)i * D, *bj = Bs + (size_t)j * D;
+      for (int t = 0; t < D; t++) y += f[t] * bj[t];
+    }
+    stf<TC>(C, (size_t)i * r + j, y);
+    lost -= y * y;
+  }
+  for (int idx = threadIdx.x; idx < b * D; idx += NT) lost += Fs[idx] * Fs[idx];
+  lost = sum64(lost);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lost;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < NT / 64; w++) t += red[w];
+    X.disc[u] = t;
+    X.sweeps[u] = 0;
+  }
+}
+
+template <typename TK, typename TC>
+__global__ void __launch_bounds__(NT) k_project(const FoldArgs a) {
+  extern __shared__ float sm[];
+  if (blockIdx.y == 0)
+    project_body<TK, TC, 0>(a, sm);
+  else
+    project_body<TK, TC, 1>(a, sm);
+}
+
 // X~ = [C B^T ; window] for one unit (section "Reconstruction and Storage").
 template <typename TC, typename TK>
 __global__ void __launch_bounds__(NT) k_reconstruct(const float *Bt, const TC *C, const TK *ring,
@@ -70,6 +125,24 @@ __global__ void k_ring_copy(uint8_t *ring, uint8_t *dense, int e, int head, int 
 }
 
 }  // namespace
+
+template <typename TK, typename TC>
+hipError_t launch_project_t(const FoldArgs &a, int nunits, hipStream_t s) {
+  const int kmax = a.k[0] > a.k[1] ? a.k[0] : a.k[1];
+  const size_t lds = sizeof(float) * ((size_t)(kmax + a.b) * D + NT / 64);
+  hipError_t e = hipFuncSetAttribute((const void *)k_project<TK, TC>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_project<TK, TC>), dim3(nunits, 2), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_project(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
+  if (kv_bf16 && coord_bf16) return launch_project_t<uint16_t, uint16_t>(a, nunits, s);
+  if (kv_bf16) return launch_project_t<uint16_t, float>(a, nunits, s);
+  if (coord_bf16) return launch_project_t<float, uint16_t>(a, nunits, s);
+  return launch_project_t<float, float>(a, nunits, s);
+}
 
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s) {
   const int row_bytes = D * (kv_bf16 ? 2 : 4);

@@ -27,11 +27,12 @@ ISKV_ERR_STATE = -7
 
 ISKV_F32 = 0
 ISKV_BF16 = 1
+MODE_JOINT, MODE_FIXED_COORDS, MODE_FIXED_BASIS = 0, 1, 2  # ISKV_MODE_* in iskv.h
 FLAG_SWEEP_CAP = 0x1
 FLAG_NONFINITE = 0x2
 
 EXPORTED = [
-    "iskv_workspace_bytes", "iskv_init", "iskv_reset", "iskv_append_block", "iskv_prefill_block",
+    "iskv_workspace_bytes", "iskv_init", "iskv_reset", "iskv_set_mode", "iskv_append_block", "iskv_prefill_block",
     "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
 ]
@@ -67,6 +68,7 @@ def load(path: str = None):
     lib.iskv_workspace_bytes.restype = ctypes.c_size_t
     lib.iskv_init.argtypes = [ctypes.POINTER(Config), _vp, ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
     lib.iskv_reset.argtypes = [_vp, _vp]
+    lib.iskv_set_mode.argtypes = [_vp, _i32]
     lib.iskv_append_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.iskv_prefill_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
     lib.iskv_decode_attn.argtypes = [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
@@ -160,6 +162,11 @@ class Cache:
     # -- API -------------------------------------------------------------
     def reset(self, stream=None):
         _check(self.lib.iskv_reset(self.h, _stream(stream)), "iskv_reset")
+
+    def set_mode(self, mode):
+        """Update mode of later folds: MODE_JOINT (the method), MODE_FIXED_COORDS
+        or MODE_FIXED_BASIS (ablations)."""
+        _check(self.lib.iskv_set_mode(self.h, int(mode)), "iskv_set_mode")
 
     def append_block(self, k_rows, v_rows, layer0=0, stream=None):
         """k_rows, v_rows: [batch, nlayers, kv_heads, nrows, 128] in kv dtype."""

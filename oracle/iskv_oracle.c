@@ -166,6 +166,10 @@ static double mgs2(double *v, const double *basis, int nb, int d) {
 /*   F       : b x d pending block                                           */
 /*   mode    : 0 = joint update of basis and coordinates (the method);       */
 /*             1 = naive: basis updated, old rows keep their coordinates     */
+/*             2 = fixed basis: once a basis exists (k > 0) it is kept;      */
+/*                 new rows are stored as their projections F B, the rank,   */
+/*                 sigma and the old rows stay, and `discarded` is the        */
+/*                 residual energy ||F - F B B^T||^2 that is lost            */
 /*   porder  : 0 = build P from the residual rows first to last, 1 = last    */
 /*             to first (a different but equally valid residual basis)       */
 /* ------------------------------------------------------------------------ */
@@ -173,6 +177,31 @@ int ora_fold(int d, int b, int r, int n, int k, double *C, int ldc, double *sigm
              double *Bt, const double *F, int mode, int porder, ora_fold_info *info) {
   if (d <= 0 || b <= 0 || r <= 0 || r > d || k < 0 || k > d || k > r || n < 0 || ldc < d)
     return ORA_ERR_ARG;
+  if (mode < 0 || mode > 2) return ORA_ERR_ARG;
+  if (mode == 2 && k > 0) {
+    /* Ablation "keeping bases fixed" ([iS-KV] Ablation Study): no residual
+     * basis and no core SVD; the block is stored in the existing basis. */
+    double lost = 0.0;
+    for (int i = 0; i < b; i++) {
+      const double *f = F + (size_t)i * d;
+      double *ci = C + (size_t)(n + i) * ldc;
+      double proj2 = 0.0;
+      for (int j = 0; j < d; j++) {
+        double y = (j < k) ? dot(f, Bt + (size_t)j * d, d) : 0.0;
+        ci[j] = y;
+        proj2 += y * y;
+      }
+      lost += dot(f, f, d) - proj2; /* B orthonormal: ||F - F B B^T||^2 */
+    }
+    if (info) {
+      info->k = k;
+      info->p = 0;
+      info->kplus = k;
+      info->sweeps = 0;
+      info->discarded = lost;
+    }
+    return ORA_OK;
+  }
   const int p = (b < d - k) ? b : d - k;
   const int m = k + b;  /* rows of Z */
   const int c = k + p;  /* columns of Z */

@@ -227,6 +227,54 @@ def test_joint_update_has_no_drift_naive_does():
     assert _drift(X, naive32) - _drift(X, joint32) > 0.1
 
 
+def test_fixed_basis_stores_projection_onto_first_basis():
+    """Ablation "keeping bases fixed" ([iS-KV] Ablation Study): after the first
+    fold, every block is stored as its orthogonal projection onto the basis of
+    that first fold (computed here with numpy from the exported basis), the
+    old rows, sigma and the rank stay, and the lost energy is ||F - F B B^T||^2."""
+    X = _rows(0, "V", 640)
+    b, r = 64, 32
+    st = oracle.UnitState.empty(D, b, r, 640)
+    st.fold(X[:b], mode=0)
+    B0 = st.Bt[:st.k].copy()
+    C0 = st.C[:b, :st.k].copy()
+    s0 = st.sigma[:st.k].copy()
+    lost = 0.0
+    for s in range(b, 640, b):
+        F = X[s:s + b]
+        info = st.fold(F, mode=2)
+        ref = F @ B0.T @ B0
+        assert info.kplus == st.k == B0.shape[0] and info.p == 0
+        assert np.allclose(st.C[s:s + b, :st.k] @ B0, ref, atol=1e-12)
+        assert np.all(st.C[s:s + b, st.k:] == 0)
+        assert abs(info.discarded - np.linalg.norm(F - ref) ** 2) <= 1e-10 * np.linalg.norm(F) ** 2
+        lost += info.discarded
+    assert np.array_equal(st.Bt[:st.k], B0) and np.array_equal(st.sigma[:st.k], s0)
+    assert np.array_equal(st.C[:b, :st.k], C0)
+    # the stored history misses exactly the energy outside span(B0) of the later
+    # blocks, plus the first fold's truncation
+    err2 = np.linalg.norm(X[:640] - st.C[:640, :st.k] @ B0) ** 2
+    assert abs(err2 - (lost + st.log[0][4])) <= 1e-9 * np.linalg.norm(X[:640]) ** 2
+
+
+def test_fixed_basis_loses_more_than_joint_update():
+    """On a stream whose dominant directions change, a frozen first-block basis
+    keeps much more error than the joint update (the pages' ablation claim,
+    qualitatively; their accuracy numbers need the model and are not used)."""
+    rng = np.random.default_rng(11)
+    W1, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    W2, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    s = np.arange(1, D + 1) ** -1.0
+    X = np.vstack([(rng.standard_normal((256, D)) * s) @ W1.T, (rng.standard_normal((512, D)) * s) @ W2.T])
+    joint = oracle.run_unit(X, D, 64, 32, 0, mode=0)
+    fixed = oracle.UnitState.empty(D, 64, 32, X.shape[0])
+    fixed.fold(X[:64], mode=0)
+    for t in range(64, X.shape[0], 64):
+        fixed.fold(X[t:t + 64], mode=2)
+    ej, ef = _drift(X, joint), _drift(X, fixed)
+    assert ef > 2 * ej and ef - ej > 0.2, (ej, ef)
+
+
 # --------------------------------------------------------------------------
 # Reconstruction, attention, storage (section "Reconstruction and Storage")
 # --------------------------------------------------------------------------
