@@ -84,7 +84,8 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
     const int r = x == 0 ? c->rank_k : c->rank_v;
     Stream &s = l.X[x];
     s.r = r;
-    s.C = take(U * l.ncap * r * cb);
+    s.cstride = (size_t)l.ncap * r + 256 / cb;
+    s.C = take(U * s.cstride * cb);
     s.Bt = (float *)take(U * r * D * 4);
     s.sig = (float *)take(U * r * 4);
     s.ring = take(U * l.rcap * D * kb);
@@ -435,7 +436,7 @@ int iskv_export_state(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t
   hipStream_t s = (hipStream_t)stream;
   const size_t cb = L.coord_bf16 ? 2 : 4;
   if (C && h->n[layer] > 0) {
-    const char *src = (const char *)X.C + (size_t)u * L.ncap * X.r * cb;
+    const char *src = (const char *)X.C + (size_t)u * X.cstride * cb;
     if (fail_hip(h, hipMemcpyAsync(C, src, (size_t)h->n[layer] * X.r * cb, hipMemcpyDeviceToDevice, s)))
       return ISKV_ERR_HIP;
   }
@@ -478,7 +479,7 @@ int iskv_import_state(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t
   hipStream_t s = (hipStream_t)stream;
   const size_t cb = L.coord_bf16 ? 2 : 4;
   if (C && h->n[layer] > 0) {
-    char *dst = (char *)X.C + (size_t)u * L.ncap * X.r * cb;
+    char *dst = (char *)X.C + (size_t)u * X.cstride * cb;
     if (fail_hip(h, hipMemcpyAsync(dst, C, (size_t)h->n[layer] * X.r * cb, hipMemcpyDeviceToDevice, s)))
       return ISKV_ERR_HIP;
   }

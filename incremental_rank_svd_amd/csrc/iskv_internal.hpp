@@ -31,7 +31,7 @@ inline int scratch_rows(int block, int rank_k, int rank_v) {
 }
 
 struct Stream {
-  void *C;          // [U][ncap][r] coordinates C = U Sigma (coord dtype), zero beyond column k
+  void *C;          // [U][cstride] coordinates C = U Sigma (coord dtype): ncap rows of r, zero beyond column k
   float *Bt;        // [U][r][D] basis vectors as rows, zero beyond row k
   float *sig;       // [U][r] singular values, zero beyond k
   void *ring;       // [U][rcap][D] exact window ring (kv dtype)
@@ -41,6 +41,8 @@ struct Stream {
   int32_t *sweeps;  // [U] core sweeps of the last fold
   float *disc;      // [U] energy dropped by the last fold
   int r;            // rank budget
+  size_t cstride;   // elements of C per unit: ncap * r plus a 256-byte pad, so unit strides are
+                    // not a power of two (all units stream the same offsets at once)
 };
 
 struct Layout {

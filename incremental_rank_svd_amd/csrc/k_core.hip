@@ -751,7 +751,7 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
   float *part = sv;  // ngrp x r partial sums (sv and sgn are dead here)
   const int ngrp = NT / r;
   {
-    TC *Cn = (TC *)X.C + ((size_t)u * a.ncap + a.n) * r;
+    TC *Cn = (TC *)X.C + (size_t)u * X.cstride + (size_t)a.n * r;
     if (tid < ngrp * r) {
       const int jr = tid % r, g0 = tid / r;
       float sq = 0.f;

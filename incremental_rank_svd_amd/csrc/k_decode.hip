@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(NT) k_decode(const DecodeArgs a) {
     }
   } else {
     const int rK = a.L.X[0].r;
-    const TC *ck = (const TC *)a.L.X[0].C + ((size_t)u * a.L.ncap + row0) * rK;
+    const TC *ck = (const TC *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride + (size_t)row0 * rK;
     for (int i = tid; i < rows; i += NT) {
       float s[MAXG];
 #pragma unroll
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(NT) k_decode(const DecodeArgs a) {
       }
     } else {
       const int rV = a.L.X[1].r;
-      const TC *cv = (const TC *)a.L.X[1].C + ((size_t)u * a.L.ncap + row0) * rV;
+      const TC *cv = (const TC *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride + (size_t)row0 * rV;
       for (int i = z; i < rows; i += nz) {
         const float x = ldf<TC>(cv, (size_t)i * rV + j);
 #pragma unroll
@@ -332,17 +332,25 @@ constexpr int WH = 2;  // window heads per pass (register budget: 128 VGPRs per 
 __host__ __device__ inline size_t decode_unit_qs(int rsK) {
   return (size_t)MAXG * (rsK > 0 ? rsK : 1) + 4 * 64 * 2 * 4 + 4 * 64 * 4;  // q', its fragments, q fragments
 }
-__host__ __device__ inline size_t decode_unit_big(int rsV, int g) {
+// nwo = waves that leave window partials: all of them on the ring path, one
+// per 32-row window step when the window is staged
+__host__ __device__ inline size_t decode_unit_big(int rsV, int g, int nwo) {
   const size_t tiles = (size_t)NWU * 32 * tile_stride(rsV) * 2 / 4;
-  const size_t comb = 2 * (size_t)NWU * MAXG + (size_t)NWU * g * rsV + (size_t)NWU * g * (2 + D) +
+  const size_t comb = 2 * (size_t)NWU * MAXG + (size_t)NWU * g * rsV + (size_t)nwo * g * (2 + D) +
                       (size_t)g * rsV + (size_t)g * D + 8 * MAXG;
   return tiles > comb ? tiles : comb;
+}
+__host__ __device__ inline int decode_unit_nwo(int ewin) {
+  const int s = (ewin + 31) / 32;
+  return (ewin > 0 && s < NWU) ? s : NWU;
 }
 // staged window rows are padded to WSTR bf16 (272 bytes): 16 lanes reading 16
 // consecutive rows then fall into distinct banks
 constexpr int WSTR = D + 8;
+// ewin = staged window rows (0: window read from the ring)
 __host__ __device__ inline size_t decode_unit_lds(int rsK, int rsV, int g, int ewin) {
-  return sizeof(float) * (decode_unit_qs(rsK) + decode_unit_big(rsV, g) + (size_t)ewin * WSTR);
+  return sizeof(float) *
+         (decode_unit_qs(rsK) + decode_unit_big(rsV, g, decode_unit_nwo(ewin)) + (size_t)ewin * WSTR);
 }
 
 // Window rows of the workgroup's window share: from the LDS copy or the ring.
@@ -544,7 +552,7 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u3
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (hq < g) {
+  if (hq < g && 32 * wv < e) {  // waves with window steps: the first decode_unit_nwo(e)
     float *w = wo + ((size_t)wv * g + hq) * (2 + D);
     if (qd == 0) {
       w[0] = m;
@@ -567,7 +575,8 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);    // [(kc*2 + part)*64 + lane]
   u32x4_t *qfrag = frag + 4 * 2 * 64;                        // [kc*64 + lane]: q itself (bf16)
   float *big = qsm + decode_unit_qs(rsK);                   // tiles, then combine scratch
-  uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g));  // [2][e][WSTR] window copy
+  const int nwo = decode_unit_nwo(a.wlds ? a.e + a.nnew : 0);
+  uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g, nwo));  // [2][e][WSTR] window copy
   int li, bi, h;
   unit_coords(a, ul, li, bi, h);
   const uint16_t *q = (const uint16_t *)a.q + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
@@ -617,8 +626,8 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   per = ((per + 31) / 32) * 32;
   const int wb = wv * per;
   const int we = min(a.n, wb + per);
-  const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.ncap * rsK;
-  const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.ncap * rsV;
+  const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride;
+  const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
   // prefetching the next step doubles the load registers: only when they fit
   constexpr bool PF = (NTV + 2 * KS) <= 6;
   u32x4_t ka[KS], kb[KS], vv[NTV];
@@ -774,8 +783,8 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   float *hm = big;                                  // [NWU][MAXG] max
   float *hl = hm + NWU * MAXG;                      // [NWU][MAXG] sum
   float *ha = hl + NWU * MAXG;                      // [NWU][g][rsV] o'
-  float *wo = ha + (size_t)NWU * g * rsV;           // [NWU][g][2 + D] window (m, l, o)
-  float *op = wo + (size_t)NWU * g * (2 + D);       // [g][rsV] merged o'
+  float *wo = ha + (size_t)NWU * g * rsV;           // [nwo][g][2 + D] window (m, l, o)
+  float *op = wo + (size_t)nwo * g * (2 + D);       // [g][rsV] merged o'
   float *ow = op + (size_t)g * rsV;                 // [g][D] merged window values
   float *fac = ow + (size_t)g * D;                  // [MAXG][8]: shift, L
   if (hq < g) {
@@ -800,14 +809,12 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   // ---- combine all waves: per head the max, the sum, o' and window values ---
   if (tid < g) {
     float M = -INFINITY;
-    for (int w = 0; w < NWU; w++) {
-      M = fmaxf(M, hm[w * MAXG + tid]);
-      M = fmaxf(M, wo[((size_t)w * g + tid) * (2 + D)]);
-    }
+    for (int w = 0; w < NWU; w++) M = fmaxf(M, hm[w * MAXG + tid]);
+    for (int w = 0; w < nwo; w++) M = fmaxf(M, wo[((size_t)w * g + tid) * (2 + D)]);
     const float ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
-    for (int w = 0; w < NWU; w++) {
-      L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+    for (int w = 0; w < NWU; w++) L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+    for (int w = 0; w < nwo; w++) {
       const float *ww = wo + ((size_t)w * g + tid) * (2 + D);
       L += __expf(ww[0] - ms) * ww[1];
     }
@@ -826,7 +833,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     const int hh = idx / D, t = idx - hh * D;
     const float ms = fac[hh * 8];
     float s = 0.f;
-    for (int w = 0; w < NWU; w++) {
+    for (int w = 0; w < nwo; w++) {
       const float *ww = wo + ((size_t)w * g + hh) * (2 + D);
       s += __expf(ww[0] - ms) * ww[2 + t];
     }

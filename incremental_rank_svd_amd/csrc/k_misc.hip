@@ -54,7 +54,7 @@ __device__ __forceinline__ void project_body(const FoldArgs &a, float *sm) {
     Fs[idx] = ldf<TK>(ring, (size_t)pos * D + t);
   }
   __syncthreads();
-  TC *C = (TC *)X.C + ((size_t)u * a.ncap + a.n) * r;
+  TC *C = (TC *)X.C + (size_t)u * X.cstride + (size_t)a.n * r;
   float lost = 0.f;
   for (int idx = threadIdx.x; idx < b * r; idx += NT) {
     const int i = idx / r, j = idx - i * r;
@@ -165,7 +165,7 @@ hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, i
   const int rows = n + e;
   if (rows == 0) return hipSuccess;
   const float *Bt = X.Bt + (size_t)u * X.r * D;
-  const size_t coff = (size_t)u * L.ncap * X.r;
+  const size_t coff = (size_t)u * X.cstride;
   const size_t roff = (size_t)u * L.rcap * D;
   if (L.coord_bf16 && L.kv_bf16)
     hipLaunchKernelGGL((k_reconstruct<uint16_t, uint16_t>), dim3(rows), dim3(NT), 0, s, Bt,

@@ -33,7 +33,7 @@ __device__ __forceinline__ void rewrite_body(const RewriteArgs &a, float *sm) {
     const int i = idx / kp, j = idx - i * kp;
     Hs[idx] = Ht[(size_t)i * r + j];
   }
-  TC *C = (TC *)X.C + (size_t)u * a.ncap * r;
+  TC *C = (TC *)X.C + (size_t)u * X.cstride;
   const int row_l = threadIdx.x & (TILE - 1);
   const int cg = threadIdx.x / TILE;  // 4 column groups
   for (int t0 = blockIdx.x * TILE; t0 < a.n; t0 += gridDim.x * TILE) {
@@ -139,7 +139,7 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
     fr[(f * 3 + 2) * 64 + lane] = u32x4_t{w2[0], w2[1], w2[2], w2[3]};
   }
   __syncthreads();
-  uint16_t *C = (uint16_t *)X.C + (size_t)u * a.ncap * r;
+  uint16_t *C = (uint16_t *)X.C + (size_t)u * X.cstride;
   const int ngroups = (a.n + 15) / 16;
   const int gstride = gridDim.x * (NT / 64);
   for (int g0 = blockIdx.x * (NT / 64) + wv; g0 < ngroups; g0 += RG * gstride) {
