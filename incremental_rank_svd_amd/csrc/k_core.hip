@@ -232,7 +232,7 @@ __device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl
           float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
           float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
           float4 xi[NQ], xj[NQ];
-          double al = 0.0, be = 0.0, ga = 0.0;
+          double al = 0.0, be = 0.0, ga = 0.0, al2 = 0.0, be2 = 0.0, ga2 = 0.0;
 #pragma unroll
           for (int e = 0; e < NQ; e++) {
             xi[e] = zi[e];
@@ -240,23 +240,37 @@ __device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl
           }
 #pragma unroll
           for (int e = 0; e < NQ; e++) {
+            // fma chains (one fp64 op per product), two per sum for latency
             const double a0 = xi[e].x, a1 = xi[e].y, a2 = xi[e].z, a3 = xi[e].w;
             const double b0 = xj[e].x, b1 = xj[e].y, b2 = xj[e].z, b3 = xj[e].w;
-            al += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
-            be += b0 * b0 + b1 * b1 + b2 * b2 + b3 * b3;
-            ga += a0 * b0 + a1 * b1 + a2 * b2 + a3 * b3;
+            al = fma(a0, a0, al);
+            al2 = fma(a1, a1, al2);
+            be = fma(b0, b0, be);
+            be2 = fma(b1, b1, be2);
+            ga = fma(a0, b0, ga);
+            ga2 = fma(a1, b1, ga2);
+            al = fma(a2, a2, al);
+            al2 = fma(a3, a3, al2);
+            be = fma(b2, b2, be);
+            be2 = fma(b3, b3, be2);
+            ga = fma(a2, b2, ga);
+            ga2 = fma(a3, b3, ga2);
           }
+          al += al2;
+          be += be2;
+          ga += ga2;
           al = quad_sum_d(al);
           be = quad_sum_d(be);
           ga = quad_sum_d(ga);
-          if (al > negl && be > negl && fabs(ga) > tol * sqrt(al * be)) {
-            const double zeta = (be - al) / (2.0 * ga);
-            const double az = fabs(zeta);
-            double td = (az > 1e150) ? 0.5 / az : 1.0 / (az + sqrt(1.0 + az * az));
-            td = copysign(td, zeta);
-            const double csd = 1.0 / sqrt(1.0 + td * td);
-            const float cs = (float)csd;
-            const float sn = (float)(csd * td);
+          if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
+            // The sums are fp64; the angle itself only needs fp32 (it is applied
+            // to fp32 columns, and cs, sn are rounded to fp32 anyway).
+            const float zeta = (float)(be - al) / (float)(2.0 * ga);
+            const float az = fabsf(zeta);
+            float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
+            t = copysignf(t, zeta);
+            const float cs = 1.f / sqrtf(1.f + t * t);
+            const float sn = cs * t;
             float4 *hi = (float4 *)(H + (size_t)ci * sj + q * rl);
             float4 *hj = (float4 *)(H + (size_t)cj * sj + q * rl);
             float4 yi[NQ], yj[NQ];
