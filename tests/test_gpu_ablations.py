@@ -89,3 +89,26 @@ def test_modes_match_oracle_and_order_drift(iskv, changing):
             assert fb > 2 * j, (x, j, fb)
         else:
             assert fb >= 0.99 * j, (x, j, fb)
+
+
+def test_mode_and_step_arguments_checked_on_host(iskv):
+    """Invalid modes and missing buffers are rejected before any device work;
+    a rejected call leaves the counters unchanged."""
+    w = replace(synth.get_config(1), layers=1, kv_heads=2, q_heads=8, decode_tokens=200, cfg_id=41)
+    cache = iskv.Cache(iskv.config_from_workload(w), device=DEV)
+    for bad in (-1, 3, 99):
+        assert cache.lib.iskv_set_mode(cache.h, bad) == iskv.ISKV_ERR_ARG
+    k = torch.zeros((1, 1, 2, 1, D), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((1, 1, 8, D), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((1, 1, 8, D), dtype=torch.float32, device=DEV)
+    vp = iskv._vp
+    f = torch.float32
+    rc = cache.lib.iskv_append_decode(cache.h, vp(k.data_ptr()), None, vp(q.data_ptr()), vp(out.data_ptr()),
+                                      0, 1, iskv.ctypes.c_float(0.1), None)
+    assert rc == iskv.ISKV_ERR_ARG and cache.counts(0) == (0, 0, 0, 0)
+    rc = cache.lib.iskv_append_decode(cache.h, vp(k.data_ptr()), vp(k.data_ptr()), vp(q.data_ptr()),
+                                      vp(out.data_ptr()), 0, 2, iskv.ctypes.c_float(0.1), None)
+    assert rc == iskv.ISKV_ERR_ARG and cache.counts(0) == (0, 0, 0, 0)  # layer range beyond the cache
+    o = cache.append_decode(k, k, q)
+    assert cache.counts(0) == (0, 1, 0, 0) and o.dtype == f and torch.isfinite(o).all()
+    cache.close()
