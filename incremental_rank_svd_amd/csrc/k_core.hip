@@ -216,14 +216,32 @@ __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols,
 // stride sj, rows split over the 4 lanes of a quad, NQ float4 chunks per
 // lane), accumulating the same rotations in H. A quad owns one pair of the
 // parallel round-robin order per round; cosines are measured from fp64 dot
-// products. Stops after a sweep without rotation or at SWEEP_CAP.
+// products. The squared column norms are kept in nrm (fp64): measured at the
+// start of every sweep and carried through each rotation by its exact effect
+// on the two norms, so a pair costs one dot product instead of three. Stops
+// after a sweep without rotation or at SWEEP_CAP.
 template <int NQ>
-__device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl, int c, int c2, double tol,
-                                              double negl, int &sweep, bool &conv) {
+__device__ __forceinline__ void jacobi_sweeps(float *J, float *H, double *nrm, int sj, int rl, int c, int c2,
+                                              double tol, double negl, int &sweep, bool &conv) {
   const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
   while (!conv && sweep < SWEEP_CAP) {
     sweep++;
     int rot = 0;
+    for (int col = qid; col < c; col += NT / 4) {
+      const float4 *zc = (const float4 *)(J + (size_t)col * sj + q * rl);
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int e = 0; e < NQ; e++) {
+        const float4 x = zc[e];
+        s0 = fma((double)x.x, (double)x.x, s0);
+        s1 = fma((double)x.y, (double)x.y, s1);
+        s0 = fma((double)x.z, (double)x.z, s0);
+        s1 = fma((double)x.w, (double)x.w, s1);
+      }
+      const double sn2 = quad_sum_d(s0 + s1);
+      if (q == 0) nrm[col] = sn2;
+    }
+    __syncthreads();
     for (int rnd = 0; rnd < c2 - 1; rnd++) {
       if (qid < c2 / 2) {
         int ci, cj;
@@ -232,7 +250,8 @@ __device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl
           float4 *zi = (float4 *)(J + (size_t)ci * sj + q * rl);
           float4 *zj = (float4 *)(J + (size_t)cj * sj + q * rl);
           float4 xi[NQ], xj[NQ];
-          double al = 0.0, be = 0.0, ga = 0.0, al2 = 0.0, be2 = 0.0, ga2 = 0.0;
+          const double al = nrm[ci], be = nrm[cj];
+          double ga = 0.0, ga2 = 0.0;
 #pragma unroll
           for (int e = 0; e < NQ; e++) {
             xi[e] = zi[e];
@@ -240,28 +259,13 @@ __device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl
           }
 #pragma unroll
           for (int e = 0; e < NQ; e++) {
-            // fma chains (one fp64 op per product), two per sum for latency
-            const double a0 = xi[e].x, a1 = xi[e].y, a2 = xi[e].z, a3 = xi[e].w;
-            const double b0 = xj[e].x, b1 = xj[e].y, b2 = xj[e].z, b3 = xj[e].w;
-            al = fma(a0, a0, al);
-            al2 = fma(a1, a1, al2);
-            be = fma(b0, b0, be);
-            be2 = fma(b1, b1, be2);
-            ga = fma(a0, b0, ga);
-            ga2 = fma(a1, b1, ga2);
-            al = fma(a2, a2, al);
-            al2 = fma(a3, a3, al2);
-            be = fma(b2, b2, be);
-            be2 = fma(b3, b3, be2);
-            ga = fma(a2, b2, ga);
-            ga2 = fma(a3, b3, ga2);
+            // fma chains (one fp64 op per product), two for latency
+            ga = fma((double)xi[e].x, (double)xj[e].x, ga);
+            ga2 = fma((double)xi[e].y, (double)xj[e].y, ga2);
+            ga = fma((double)xi[e].z, (double)xj[e].z, ga);
+            ga2 = fma((double)xi[e].w, (double)xj[e].w, ga2);
           }
-          al += al2;
-          be += be2;
-          ga += ga2;
-          al = quad_sum_d(al);
-          be = quad_sum_d(be);
-          ga = quad_sum_d(ga);
+          ga = quad_sum_d(ga + ga2);
           if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
             // The sums are fp64; the angle itself only needs fp32 (it is applied
             // to fp32 columns, and cs, sn are rounded to fp32 anyway).
@@ -294,6 +298,12 @@ __device__ __forceinline__ void jacobi_sweeps(float *J, float *H, int sj, int rl
                              cs * u0.w - sn * u1.w};
               hj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
                              sn * u0.w + cs * u1.w};
+            }
+            if (q == 0) {
+              // norms of the rotated pair, from the rotation actually applied
+              const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
+              nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
+              nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
             }
             rot = 1;
           }
@@ -520,19 +530,20 @@ __device__ __forceinline__ void core_body(const FoldArgs &a, float *smem) {
     const double negl = (double)(ntol * ntol * fro2);
     __syncthreads();  // sv is reused below
     const int c2 = c + (c & 1);
+    double *nrm = (double *)tau;  // c squared column norms (tau and sv are free during the sweeps)
     int sweep = 0;
     bool conv = (c < 2);
     // rows per quad lane as a compile-time constant: the loads of a column
     // are then issued back to back
     switch (rl / 4) {
-      case 1: jacobi_sweeps<1>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 2: jacobi_sweeps<2>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 3: jacobi_sweeps<3>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 4: jacobi_sweeps<4>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 5: jacobi_sweeps<5>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 6: jacobi_sweeps<6>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      case 7: jacobi_sweeps<7>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
-      default: jacobi_sweeps<8>(J, H, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 1: jacobi_sweeps<1>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 2: jacobi_sweeps<2>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 3: jacobi_sweeps<3>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 4: jacobi_sweeps<4>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 5: jacobi_sweeps<5>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 6: jacobi_sweeps<6>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      case 7: jacobi_sweeps<7>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
+      default: jacobi_sweeps<8>(J, H, nrm, sj, rl, c, c2, tol, negl, sweep, conv); break;
     }
     if (tid == 0) {
       if (!conv) atomicOr(a.status, FLAG_SWEEP_CAP);

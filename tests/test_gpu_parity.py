@@ -273,6 +273,30 @@ def test_zero_rows_and_nan_flag(iskv):
     assert cache2.status() & iskv.FLAG_NONFINITE
 
 
+def test_rank_deficient_rows(iskv):
+    """Rows of rank 3 under a rank budget of 8: five kept singular values are
+    at the rounding level, so the core takes its rotation-accumulating route;
+    the basis stays orthonormal and the history matches the oracle."""
+    from dataclasses import replace
+
+    w = replace(synth.get_config(0), decode_tokens=400, rank_k=8, cfg_id=16)
+    rows = _rows_all(w, w.total_tokens)
+    rng = np.random.default_rng(77)
+    rows["K"][0, 0, 0] = rng.standard_normal((w.total_tokens, 3)) @ rng.standard_normal((3, D))
+    cache = _cache(iskv, w)
+    _feed(cache, w, rows, 0, 400, 16)
+    assert cache.status() == 0
+    st = oracle_units([(rows["K"][0, 0, 0], w.block, w.rank_k, w.window, 0)])
+    C, sig, Bt, W, n, e, k = unit_state(cache, 0, 0, 0, 0)
+    assert k == 8
+    assert np.abs(Bt[:k] @ Bt[:k].T - np.eye(k)).max() < 1e-4
+    np.testing.assert_allclose(sig[:3], st[0].sigma[:3], rtol=1e-4)
+    assert sig[3:k].max() <= 1e-4 * sig[0]
+    rec = cache.reconstruct(0, 0, 0, 0).cpu().double().numpy()
+    ref = st[0].reconstruct()
+    assert np.linalg.norm(rec - ref) <= 1e-4 * np.linalg.norm(ref)
+
+
 def test_deterministic_and_checkpoint_resume(iskv):
     """Two identical runs are bitwise equal; exporting every unit's state into a
     fresh cache and continuing gives the same bits as an uninterrupted run."""
