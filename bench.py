@@ -35,7 +35,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--workload", default="llama3_8b_gqa_8k")
     p.add_argument("--tokens", type=int, default=0, help="override decode tokens (profiling runs)")
-    p.add_argument("--sample-every", type=int, default=16, help="event-time every n-th decode launch")
+    p.add_argument("--sample-every", type=int, default=1,
+                   help="event-time every n-th run of decode launches between two folds")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (default: one per core, <= 32)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -166,11 +167,18 @@ def main():
     n_sample = max(1, args.sample_every)
 
     def run_step(sampled):
+        """One pass of the whole path over the T tokens. With `sampled`, the
+        runs of consecutive non-folding tokens (the launches between two folds)
+        are bracketed by one pair of events each: kernels on the stream run
+        back to back, so a run's elapsed time over its launch count is the
+        kernel's average duration, without a per-launch event overhead."""
         if lib.iskv_reset(h, sp) != 0:
             raise RuntimeError("reset failed")
         n = e = kK = kV = 0
         b, wnd = w.block, w.window
         ev = []
+        seg = None  # [start event, bytes, launches] of the open run
+        nseg = 0
         for t in range(T):
             e += 1
             folds = e >= wnd + b  # this token's append folds: the call runs ingest, fold, decode
@@ -182,17 +190,29 @@ def main():
                 n += b
                 e -= b
             args = (h, VP(kp0 + t * kstr), VP(vp0 + t * kstr), VP(qp0 + t * qstr), op, 0, L, scale, sp)
-            if sampled is not None and not folds and t % n_sample == 0:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                rc = step_call(*args)
-                e1.record(stream)
-                ev.append((e0, e1, decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, appended=1)))
-            else:
-                rc = step_call(*args)
+            if sampled is not None:
+                if folds and seg is not None:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    ev.append((seg[0], e1, seg[1], seg[2]))
+                    seg = None
+                if not folds:
+                    if seg is None and nseg % n_sample == 0:
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        seg = [e0, 0, 0]
+                    if seg is not None:
+                        seg[1] += decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, appended=1)
+                        seg[2] += 1
+                if folds:
+                    nseg += 1
+            rc = step_call(*args)
             if rc:
                 raise RuntimeError("append_decode failed: %d" % rc)
+        if seg is not None:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            ev.append((seg[0], e1, seg[1], seg[2]))
         if sampled is not None:
             sampled.extend(ev)
         return n
@@ -219,7 +239,8 @@ def main():
 
     dec_ms = [s[0].elapsed_time(s[1]) for s in samples]
     dec_bytes = sum(s[2] for s in samples)
-    dec_avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
+    dec_launches = sum(s[3] for s in samples)
+    dec_avg_us = 1e3 * sum(dec_ms) / dec_launches
     achieved = dec_bytes / (sum(dec_ms) * 1e-3) / 1e9
     dec_share = (dec_avg_us * 1e-6 * T) / step_s
 
@@ -272,7 +293,7 @@ def main():
                               "GBps": final_bytes / (final_ms * 1e-3) / 1e9},
         "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "avg_launch_us": dec_avg_us, "launches_sampled": len(dec_ms),
+                     "avg_launch_us": dec_avg_us, "launches_sampled": dec_launches,
                      "share_of_step": dec_share},
     }
     if not args.no_cpu_baseline:
