@@ -117,6 +117,18 @@ ISKV_API int iskv_set_mode(iskv_t h, int32_t mode);
 ISKV_API int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows,
                       int32_t layer0, int32_t nlayers, void *stream);
 
+/* One-shot prompt compression (section "Prefill Compression"; key and value
+ * protection not modelled): the nrows (>= 1) rows per sequence and kv head
+ * of layers layer0..layer0+nlayers-1 are factorised at once by a truncated
+ * SVD and become the whole history, k = min(r, nrows, d) per stream
+ * (section "Theoretical Foundation"); the window stays empty. k_rows,
+ * v_rows: [batch][nlayers][kv_heads][nrows][d] in kv_dtype, device memory,
+ * read only. Requires every such layer to be empty (n == 0 and e == 0, else
+ * ISKV_ERR_STATE) and nrows <= max_tokens (else ISKV_ERR_CAPACITY). Later
+ * appends fold into this history as usual. */
+ISKV_API int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows,
+                                  int32_t layer0, int32_t nlayers, void *stream);
+
 /* Prompt compression without a window: fold exactly b rows per sequence and
  * kv head straight into the history of layers layer0..layer0+nlayers-1.
  * Requires every such layer's window to be empty (e == 0). Layout as in

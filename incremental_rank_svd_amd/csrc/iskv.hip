@@ -5,6 +5,7 @@
 // Updates" (the oldest b rows become the pending block F once the window
 // holds w + b rows).
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "iskv.h"
@@ -320,6 +321,46 @@ int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t
     for (int l = l0; l < l1; l++) h->e[l] += b;
     rc = fold_run(h, l0, l1, s);
     if (rc) return rc;
+    l0 = l1;
+  }
+  return ISKV_OK;
+}
+
+int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows, int32_t layer0,
+                         int32_t nlayers, void *stream) {
+  if (!h || !k_rows || !v_rows) return ISKV_ERR_ARG;
+  if (h->poisoned) return ISKV_ERR_POISONED;
+  if (bad_layers(h, layer0, nlayers) || nrows < 1) return ISKV_ERR_ARG;
+  for (int l = layer0; l < layer0 + nlayers; l++) {
+    if (h->n[l] != 0 || h->e[l] != 0) return ISKV_ERR_STATE;
+    if ((long long)nrows > h->cfg.max_tokens || nrows > h->L.ncap) return ISKV_ERR_CAPACITY;
+  }
+  const Layout &L = h->L;
+  hipStream_t s = (hipStream_t)stream;
+  const int per_layer = L.batch * L.kvh;
+  for (int l0 = layer0; l0 < layer0 + nlayers;) {
+    const int l1 = run_end(h, l0, layer0 + nlayers);
+    OneshotArgs a = {};
+    for (int x = 0; x < 2; x++) a.X[x] = L.X[x];
+    a.src[0] = k_rows;
+    a.src[1] = v_rows;
+    a.batch = L.batch;
+    a.kvh = L.kvh;
+    a.nl_in = nlayers;
+    a.lrel0 = l0 - layer0;
+    a.nl = l1 - l0;
+    a.u0 = l0 * per_layer;
+    a.nrows = nrows;
+    a.status = L.status;
+    int rc = fail_hip(h, launch_oneshot(a, (l1 - l0) * per_layer, L.kv_bf16, L.coord_bf16, s));
+    if (rc) return rc;
+    for (int l = l0; l < l1; l++) {
+      h->n[l] = nrows;
+      h->e[l] = 0;
+      h->head[l] = 0;
+      h->kk[l] = std::min(std::min(L.X[0].r, (int)nrows), D);
+      h->kv[l] = std::min(std::min(L.X[1].r, (int)nrows), D);
+    }
     l0 = l1;
   }
   return ISKV_OK;

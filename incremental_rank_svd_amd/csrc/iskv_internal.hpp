@@ -102,6 +102,15 @@ struct DecodeArgs {
   int nnew;
 };
 
+// One-shot prefill of a layer run: every unit's nrows prompt rows
+struct OneshotArgs {
+  Stream X[2];
+  const void *src[2];  // K, V rows [batch][nl_in][kvh][nrows][D]
+  int batch, kvh, nl_in, lrel0, nl;
+  int u0, nrows;
+  uint32_t *status;
+};
+
 // ---------------------------------------------------------------------------
 // device helpers
 // ---------------------------------------------------------------------------
@@ -164,6 +173,8 @@ hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 // fixed-basis fold: new rows C[n + i] = F_i B (k columns), discarded energy
 hipError_t launch_project(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+// one-shot prefill: QR + Jacobi (k_oneshot_svd), then coordinates and sigma (k_oneshot_coords)
+hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 // true when launch_decode can take the appended row itself (nnew = 1)
 bool decode_can_fuse(const DecodeArgs &a);
 int decode_chunk_rows(const Layout &L);  // history rows per decode block

@@ -845,6 +845,290 @@ hipError_t launch_core_nr(const FoldArgs &a, int nunits, hipStream_t s) {
   return launch_core_t<8, TK, TC>(a, nunits, s);
 }
 
+// ---------------------------------------------------------------------------
+// One-shot prefill ([iS-KV] Prefill Compression: the prompt's rows of a unit
+// factorised at once by a truncated SVD, k = min(r, rows, d)). The SVD goes
+// through the R factor: the rows are taken 128 at a time and folded into R
+// by a Householder QR of [R; rows] (R keeps the right singular vectors and
+// singular values of all rows seen). Then the columns of R^T (the rows of R)
+// are orthogonalised by the same one-sided Jacobi as the fold's core: R^T H
+// = V Sigma, so each kept right singular vector is a converged column over
+// its norm. Rows of R beyond the rank of the rows are rounding noise and stay
+// frozen as negligible columns, so no real content is left behind in them
+// (orthogonalising the columns of R instead would freeze shrinking columns
+// that still hold content at the threshold's level). The kept vectors,
+// signed by the sign rule, become the basis; k_oneshot_coords then stores
+// the coordinates C = X B and sigma as their column norms.
+// ---------------------------------------------------------------------------
+constexpr int OS_M = 2 * D;  // rows of [R; block]
+
+__host__ __device__ inline int oneshot_small() {  // float offset of tau, sv, sgn, perm
+  const int z = D * ldz(OS_M);
+  const int jh = 2 * D * jac_stride(D);
+  return z > jh ? z : jh;
+}
+
+template <typename TK, int XK>
+__device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
+  const Stream &X = a.X[XK];
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2, lane = tid & 63, wv = tid >> 6;
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int lrel = ul / (a.batch * a.kvh), rem = ul - lrel * (a.batch * a.kvh);
+  const int bi = rem / a.kvh, hh = rem - bi * a.kvh;
+  const TK *src = (const TK *)a.src[XK] +
+                  (((size_t)bi * a.nl_in + a.lrel0 + lrel) * a.kvh + hh) * (size_t)a.nrows * D;
+  const int r = X.r;
+  const int kplus = min(min(r, a.nrows), D);
+  float *tau = smem + oneshot_small();
+  float *sv = tau + D;
+  float *sgn = sv + D;
+  int *perm = (int *)(sgn + D);
+  float *Zb = smem;
+  const int mz = ldz(OS_M);
+  for (int idx = tid; idx < D * mz; idx += NT) Zb[idx] = 0.f;
+  __syncthreads();
+  for (int r0 = 0; r0 < a.nrows; r0 += D) {
+    // rows r0 .. r0+127 below R (zero past the last row)
+    for (int idx = tid; idx < D * D; idx += NT) {
+      const int i = idx / D, t = idx - i * D;
+      Zb[(size_t)t * mz + D + i] = (r0 + i < a.nrows) ? ldf<TK>(src, (size_t)(r0 + i) * D + t) : 0.f;
+    }
+    __syncthreads();
+    house_qr<OS_M / 4, false>(Zb, mz, OS_M, D, D, tau);
+    // keep R: clear the reflectors below its diagonal and the block rows
+    for (int idx = tid; idx < D * OS_M; idx += NT) {
+      const int col = idx / OS_M, row = idx - col * OS_M;
+      if (row > col) Zb[(size_t)col * mz + row] = 0.f;
+    }
+    __syncthreads();
+  }
+  // R^T (R's rows as columns) into the Jacobi layout through registers, H = I
+  const int c = D, sj = jac_stride(D), rl = jac_rl(D);
+  float *J = smem, *H = smem + c * sj;
+  {
+    constexpr int PER = (D * (D + 1) / 2 + NT - 1) / NT;
+    const int ntri = D * (D + 1) / 2;
+    float hold[PER];
+#pragma unroll
+    for (int z = 0; z < PER; z++) {
+      const int e = tid + NT * z;
+      hold[z] = 0.f;
+      if (e < ntri) {
+        int col, row;
+        tri_index(e, col, row);
+        hold[z] = Zb[(size_t)col * mz + row];
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < c * sj; idx += NT) {
+      const int col = idx / sj, row = idx - col * sj;
+      J[idx] = 0.f;
+      H[idx] = (row == col) ? 1.f : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int z = 0; z < PER; z++) {
+      const int e = tid + NT * z;
+      if (e < ntri) {
+        int col, row;
+        tri_index(e, col, row);
+        J[(size_t)row * sj + col] = hold[z];
+      }
+    }
+    __syncthreads();
+  }
+  double negl;
+  {
+    float fr = 0.f;
+    for (int idx = tid; idx < c * sj; idx += NT) fr += J[idx] * J[idx];
+    fr = sum64(fr);
+    if (lane == 0) sv[wv] = fr;
+    __syncthreads();
+    const float fro2 = sv[0] + sv[1] + sv[2] + sv[3];
+    const double tol = 8.0 * 5.9604644775390625e-8;
+    const float ntol = (float)c * 5.9604645e-8f;
+    negl = (double)(ntol * ntol * fro2);
+    __syncthreads();
+    double *nrm = (double *)tau;
+    int sweep = 0;
+    bool conv = false;
+    jacobi_sweeps<D / 16>(J, H, nrm, sj, rl, c, c, tol, negl, sweep, conv);
+    if (tid == 0) {
+      if (!conv) atomicOr(a.status, FLAG_SWEEP_CAP);
+      X.sweeps[u] = sweep;
+    }
+  }
+  // singular values, rank order (non-finite ones flagged and ranked last)
+  for (int col = qid; col < c; col += NT / 4) {
+    const float *zc = J + (size_t)col * sj + q * rl;
+    float s = 0.f;
+    for (int e = 0; e < rl; e++) s += zc[e] * zc[e];
+    s = quad_sum(s);
+    if (q == 0) {
+      float v = sqrtf(s);
+      if (!(v <= 3.0e38f)) {
+        atomicOr(a.status, FLAG_NONFINITE);
+        v = -1.f;
+      }
+      sv[col] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < c) {
+    const float me = sv[tid];
+    int rank = 0;
+    for (int i = 0; i < c; i++) {
+      const float o = sv[i];
+      rank += (o > me || (o == me && i < tid)) ? 1 : 0;
+    }
+    perm[rank] = tid;
+  }
+  __syncthreads();
+  // basis rows, staged in the H region (free now): converged column perm[jr]
+  // over its norm; a kept column at the rounding level (rows of rank below k)
+  // is completed instead by the first unit vector e_t that keeps a norm above
+  // 1/2 after two Gram-Schmidt passes against the rows before it
+  float *Bs = H;  // r x D
+  const float neglf = (float)negl;
+  for (int idx = tid; idx < kplus * D; idx += NT) {
+    const int jr = idx / D, t = idx - jr * D;
+    const int col = perm[jr];
+    const float sc = sv[col];
+    Bs[idx] = (sc * sc > neglf) ? J[(size_t)col * sj + t] / sc : 0.f;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int t_next = 0;
+    for (int jr = 0; jr < kplus; jr++) {
+      const float sc = sv[perm[jr]];
+      if (sc * sc > neglf) continue;
+      for (; t_next < D; t_next++) {
+        float w0 = (lane == t_next) ? 1.f : 0.f, w1 = (lane + 64 == t_next) ? 1.f : 0.f;
+        for (int pass = 0; pass < 2; pass++) {
+          for (int i = 0; i < kplus; i++) {
+            if (i == jr) continue;
+            const float b0 = Bs[(size_t)i * D + lane], b1 = Bs[(size_t)i * D + lane + 64];
+            const float pr = sum64(w0 * b0 + w1 * b1);
+            w0 -= pr * b0;
+            w1 -= pr * b1;
+          }
+        }
+        const float nn = sqrtf(sum64(w0 * w0 + w1 * w1));
+        if (nn > 0.5f) {
+          Bs[(size_t)jr * D + lane] = w0 / nn;
+          Bs[(size_t)jr * D + lane + 64] = w1 / nn;
+          t_next++;
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // sign rule: the entry of largest magnitude (lowest index on ties) of each
+  // basis vector is positive; one wave per row
+  float *Btw = X.Bt + (size_t)u * r * D;
+  for (int jr = wv; jr < r; jr += NT / 64) {
+    if (jr < kplus) {
+      const float h0 = Bs[(size_t)jr * D + lane], h1 = Bs[(size_t)jr * D + lane + 64];
+      float best = fabsf(h0);
+      int bi2 = lane;
+      if (fabsf(h1) > best) {
+        best = fabsf(h1);
+        bi2 = lane + 64;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi2, off);
+        if (ob > best || (ob == best && oi < bi2)) {
+          best = ob;
+          bi2 = oi;
+        }
+      }
+      const float sg = (Bs[(size_t)jr * D + bi2] < 0.f) ? -1.f : 1.f;
+      Btw[(size_t)jr * D + lane] = sg * h0;
+      Btw[(size_t)jr * D + lane + 64] = sg * h1;
+    } else {
+      Btw[(size_t)jr * D + lane] = 0.f;
+      Btw[(size_t)jr * D + lane + 64] = 0.f;
+    }
+  }
+  if (tid == 0) {
+    float dsum = 0.f;
+    for (int i = kplus; i < c; i++) dsum += sv[perm[i]] * sv[perm[i]];
+    X.disc[u] = dsum;
+  }
+}
+
+// one workgroup per CU (its LDS is 136 KB), so each wave may take the whole
+// register file
+template <typename TK>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) k_oneshot_svd(const OneshotArgs a) {
+  extern __shared__ float smem[];
+  if (blockIdx.y == 0)
+    oneshot_svd_body<TK, 0>(a, smem);
+  else
+    oneshot_svd_body<TK, 1>(a, smem);
+}
+
+// C[i] = X_i B (kplus columns, zero to r) for every prompt row; sigma = the
+// column norms of the coordinates as stored. Rows are staged in LDS NT / r at
+// a time; thread (g, j) owns column j of row g of each pass.
+template <typename TK, typename TC>
+__global__ void __launch_bounds__(NT) k_oneshot_coords(const OneshotArgs a) {
+  extern __shared__ float smem[];
+  const int XK = blockIdx.y;
+  const Stream &X = a.X[XK];
+  const int tid = threadIdx.x;
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int lrel = ul / (a.batch * a.kvh), rem = ul - lrel * (a.batch * a.kvh);
+  const int bi = rem / a.kvh, hh = rem - bi * a.kvh;
+  const TK *src = (const TK *)a.src[XK] +
+                  (((size_t)bi * a.nl_in + a.lrel0 + lrel) * a.kvh + hh) * (size_t)a.nrows * D;
+  const int r = X.r;
+  const int kplus = min(min(r, a.nrows), D);
+  const int G = NT / r;  // rows per pass
+  float *Bs = smem;                      // r x (D + 1)
+  float *xs = Bs + (size_t)r * (D + 1);  // G x D
+  float *part = xs + (size_t)G * D;      // G x r
+  const float *Bt = X.Bt + (size_t)u * r * D;
+  for (int idx = tid; idx < r * D; idx += NT) {
+    const int j = idx / D, t = idx - j * D;
+    Bs[j * (D + 1) + t] = Bt[idx];
+  }
+  TC *Cu = (TC *)X.C + (size_t)u * X.cstride;
+  const int g0 = tid / r, j = tid - g0 * r;
+  float sq = 0.f;
+  for (int i0 = 0; i0 < a.nrows; i0 += G) {
+    __syncthreads();  // xs free (and Bs written, first pass)
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int g = idx / D, t = idx - g * D;
+      xs[idx] = (i0 + g < a.nrows) ? ldf<TK>(src, (size_t)(i0 + g) * D + t) : 0.f;
+    }
+    __syncthreads();
+    const int i = i0 + g0;
+    if (g0 < G && i < a.nrows) {
+      float s = 0.f;
+      if (j < kplus) {
+        const float *xr = xs + (size_t)g0 * D, *br = Bs + (size_t)j * (D + 1);
+#pragma unroll 8
+        for (int t = 0; t < D; t++) s += xr[t] * br[t];
+      }
+      stf<TC>(Cu, (size_t)i * r + j, s);
+      const float st = ldf<TC>(Cu, (size_t)i * r + j);
+      sq += st * st;
+    }
+  }
+  __syncthreads();
+  if (g0 < G) part[g0 * r + j] = sq;
+  __syncthreads();
+  if (tid < r) {
+    float s2 = 0.f;
+    for (int g = 0; g < G; g++) s2 += part[g * r + tid];
+    X.sig[(size_t)u * r + tid] = (tid < kplus) ? sqrtf(s2) : 0.f;
+  }
+}
+
 }  // namespace
 
 size_t core_lds_bytes(int k, int b, int r) {
@@ -858,6 +1142,35 @@ hipError_t launch_core(const FoldArgs &a0, int nunits, int kv_bf16, int coord_bf
   if (kv_bf16 && !coord_bf16) return launch_core_nr<uint16_t, float>(a, nunits, s);
   if (!kv_bf16 && coord_bf16) return launch_core_nr<float, uint16_t>(a, nunits, s);
   return launch_core_nr<float, float>(a, nunits, s);
+}
+
+hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
+  const size_t lds1 = sizeof(float) * ((size_t)oneshot_small() + 4 * D);
+  hipError_t e;
+  if (kv_bf16) {
+    e = hipFuncSetAttribute((const void *)k_oneshot_svd<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_oneshot_svd<uint16_t>, dim3(nunits, 2), dim3(NT), lds1, s, a);
+  } else {
+    e = hipFuncSetAttribute((const void *)k_oneshot_svd<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_oneshot_svd<float>, dim3(nunits, 2), dim3(NT), lds1, s, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rmin = a.X[0].r < a.X[1].r ? a.X[0].r : a.X[1].r;
+  const int rmax = a.X[0].r > a.X[1].r ? a.X[0].r : a.X[1].r;
+  const size_t lds2 = sizeof(float) * ((size_t)rmax * (D + 1) + (size_t)(NT / rmin) * D + NT);
+  auto go = [&](const void *kf, auto kern) {
+    hipError_t e2 = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL(kern, dim3(nunits, 2), dim3(NT), lds2, s, a);
+    return hipGetLastError();
+  };
+  if (kv_bf16 && coord_bf16) return go((const void *)k_oneshot_coords<uint16_t, uint16_t>, k_oneshot_coords<uint16_t, uint16_t>);
+  if (kv_bf16) return go((const void *)k_oneshot_coords<uint16_t, float>, k_oneshot_coords<uint16_t, float>);
+  if (coord_bf16) return go((const void *)k_oneshot_coords<float, uint16_t>, k_oneshot_coords<float, uint16_t>);
+  return go((const void *)k_oneshot_coords<float, float>, k_oneshot_coords<float, float>);
 }
 
 }  // namespace iskv

@@ -33,6 +33,7 @@ FLAG_NONFINITE = 0x2
 
 EXPORTED = [
     "iskv_workspace_bytes", "iskv_init", "iskv_reset", "iskv_set_mode", "iskv_append_block", "iskv_prefill_block",
+    "iskv_prefill_oneshot",
     "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
 ]
@@ -188,6 +189,17 @@ class Cache:
         vp = self._t(v_rows, shape, self.kv_dtype, "v_rows")
         _check(self.lib.iskv_prefill_block(self.h, kp, vp, layer0, nl, _stream(stream)),
                "iskv_prefill_block")
+
+    def prefill_oneshot(self, k_rows, v_rows, layer0=0, stream=None):
+        """All prompt rows [batch, nlayers, kv_heads, nrows, 128] factorised at
+        once into the (empty) history of those layers."""
+        c = self.cfg
+        nl, nrows = k_rows.shape[1], k_rows.shape[3]
+        shape = (c.batch, nl, c.kv_heads, nrows, c.head_dim)
+        kp = self._t(k_rows, shape, self.kv_dtype, "k_rows")
+        vp = self._t(v_rows, shape, self.kv_dtype, "v_rows")
+        _check(self.lib.iskv_prefill_oneshot(self.h, kp, vp, nrows, layer0, nl, _stream(stream)),
+               "iskv_prefill_oneshot")
 
     def decode_attn(self, q, out=None, layer0=0, scale=None, stream=None):
         """q: [batch, nlayers, q_heads, 128] in kv dtype; returns fp32 out of the same shape."""

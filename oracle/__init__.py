@@ -69,6 +69,9 @@ def _bind(lib):
     lib.ora_attend.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D, _D,
                                ctypes.c_double, _D]
     lib.ora_attend.restype = None
+    lib.ora_prefill_oneshot.argtypes = [ctypes.c_int] * 3 + [_D, _D, ctypes.c_int, _D, _D,
+                                                              ctypes.POINTER(_FoldInfo)]
+    lib.ora_prefill_oneshot.restype = ctypes.c_int
     lib.ora_storage_bytes.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double]
     lib.ora_storage_bytes.restype = ctypes.c_double
     return lib
@@ -193,6 +196,25 @@ class UnitState:
         assert rows.shape[0] % self.b == 0
         for s in range(0, rows.shape[0], self.b):
             self.fold(rows[s: s + self.b], mode=mode, lib=lib)
+
+    def prefill_oneshot(self, rows, lib=None):
+        """Factorise all prompt rows at once into the history (the cache must
+        be empty): truncated SVD, k = min(r, rows, d)."""
+        assert self.n == 0 and not self.window
+        lib = lib or load()
+        rows = _f64(rows).reshape(-1, self.d)
+        N = rows.shape[0]
+        if self.C.shape[0] < N + self.b:
+            self.C = np.zeros((N + self.b, self.d))
+        info = _FoldInfo()
+        kp = lib.ora_prefill_oneshot(self.d, self.r, N, _p(rows), _p(self.C), self.d, _p(self.sigma),
+                                     _p(self.Bt), ctypes.byref(info))
+        if kp < 0:
+            raise OracleError("ora_prefill_oneshot failed: %d" % kp)
+        self.log.append((info.k, info.p, info.kplus, info.sweeps, info.discarded))
+        self.n = N
+        self.k = kp
+        return info
 
     def history(self):
         """History coordinates and basis: (C[:n, :k], sigma[:k], Bt[:k])."""

@@ -396,6 +396,79 @@ out:
 }
 
 /* ------------------------------------------------------------------------ */
+/* One-shot prefill (section "Prefill Compression": the prompt's rows are    */
+/* factorised at once by a truncated SVD; key and value protection are not  */
+/* modelled, so every row goes to the history).                              */
+/*   X     : N x d prompt rows, row-major                                    */
+/*   C     : N x ldc (ldc >= d); on return rows hold U_r Sigma_r in columns  */
+/*           0..kplus-1, zeros beyond                                        */
+/*   sigma : d; Bt : d x d (rows 0..kplus-1 = right singular vectors, each   */
+/*           signed so that its entry of largest magnitude is positive)      */
+/* kplus = min(r, N, d) (section "Theoretical Foundation": SVD_r keeps       */
+/* k = min(r, n, d)). The SVD is the same one-sided Jacobi as the fold's     */
+/* core, applied to X itself (padded with zero rows to d rows when N < d,    */
+/* which changes neither the singular values nor the right vectors).         */
+/* info (optional): k = 0, p = N, kplus, sweeps, discarded energy.           */
+/* Returns kplus, or a negative error.                                       */
+/* ------------------------------------------------------------------------ */
+int ora_prefill_oneshot(int d, int r, int N, const double *X, double *C, int ldc, double *sigma,
+                        double *Bt, ora_fold_info *info) {
+  if (d <= 0 || r <= 0 || N <= 0 || ldc < d) return ORA_ERR_ARG;
+  const int m = N > d ? N : d;
+  const int kplus = (r < N ? r : N) < d ? (r < N ? r : N) : d;
+  int rc = 0;
+  double *Z = calloc((size_t)m * d, sizeof(double));
+  double *H = calloc((size_t)d * d, sizeof(double));
+  double *sv = calloc((size_t)d, sizeof(double));
+  int *perm = calloc((size_t)d, sizeof(int));
+  double *sgn = calloc((size_t)d, sizeof(double));
+  if (!Z || !H || !sv || !perm || !sgn) { rc = ORA_ERR_MEM; goto out; }
+  /* Z = X column-major (column t holds feature t of every row) */
+  for (int i = 0; i < N; i++)
+    for (int t = 0; t < d; t++) Z[(size_t)t * m + i] = X[(size_t)i * d + t];
+  {
+    int sw = ora_jacobi(m, d, Z, H, sv, 60);
+    if (sw < 0) { rc = ORA_ERR_NOCONV; goto out; }
+    if (info) info->sweeps = sw;
+  }
+  for (int j = 0; j < d; j++) perm[j] = j;
+  for (int a = 1; a < d; a++) {
+    int pj = perm[a];
+    int q = a - 1;
+    while (q >= 0 && sv[perm[q]] < sv[pj]) { perm[q + 1] = perm[q]; q--; }
+    perm[q + 1] = pj;
+  }
+  /* basis vector jj = column perm[jj] of H = V, signed by its largest entry */
+  for (int jj = 0; jj < d; jj++) {
+    const double *h = H + (size_t)perm[jj] * d;
+    int am = 0;
+    for (int t = 1; t < d; t++)
+      if (fabs(h[t]) > fabs(h[am])) am = t;
+    sgn[jj] = (h[am] < 0.0) ? -1.0 : 1.0;
+    for (int t = 0; t < d; t++) Bt[(size_t)jj * d + t] = (jj < kplus) ? sgn[jj] * h[t] : 0.0;
+  }
+  /* U_r Sigma_r = X V_r: the rotated columns (X H) of the kept components */
+  for (int i = 0; i < N; i++)
+    for (int jj = 0; jj < ldc; jj++)
+      C[(size_t)i * ldc + jj] = (jj < kplus) ? sgn[jj] * Z[(size_t)perm[jj] * m + i] : 0.0;
+  {
+    double disc = 0.0;
+    for (int jj = kplus; jj < d; jj++) disc += sv[perm[jj]] * sv[perm[jj]];
+    for (int jj = 0; jj < d; jj++) sigma[jj] = (jj < kplus) ? sv[perm[jj]] : 0.0;
+    if (info) {
+      info->k = 0;
+      info->p = N;
+      info->kplus = kplus;
+      info->discarded = disc;
+    }
+  }
+  rc = kplus;
+out:
+  free(Z); free(H); free(sv); free(perm); free(sgn);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Whole stream of one unit (section "Architecture Overview": exact recent   */
 /* window of w rows plus low-rank history).                                  */
 /*   X        : N x d rows in arrival order                                  */

@@ -118,6 +118,7 @@ def test_null_handle_and_strerror(lib):
     assert lib.iskv_set_mode(None, iskv.MODE_JOINT) == iskv.ISKV_ERR_ARG
     assert lib.iskv_append_decode(None, None, None, None, None, 0, 1, ctypes.c_float(1.0), None) == iskv.ISKV_ERR_ARG
     assert lib.iskv_decode_attn(None, None, None, 0, 1, ctypes.c_float(1.0), None) == iskv.ISKV_ERR_ARG
+    assert lib.iskv_prefill_oneshot(None, None, None, 16, 0, 1, None) == iskv.ISKV_ERR_ARG
     for code in range(0, -8, -1):
         assert lib.iskv_strerror(code) not in (None, b"", b"unknown status")
     assert lib.iskv_strerror(-99) == b"unknown status"

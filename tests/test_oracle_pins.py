@@ -341,3 +341,55 @@ def test_window_policy_counts_match_workloads():
     assert synth.get_config(1).final_counts() == (8064, 128, 126)
     assert synth.get_config(3).final_counts() == (66432, 128, 1038)
     assert synth.get_config(4).final_counts() == (16128, 256, 126)
+
+
+# --------------------------------------------------------------------------
+# One-shot prefill (page "iS-KV ...", section "Prefill Compression": a
+# truncated SVD of the prompt rows; k = min(r, n, d) per "Theoretical
+# Foundation")
+# --------------------------------------------------------------------------
+
+def test_oneshot_prefill_is_the_truncated_svd():
+    rng = np.random.default_rng(11)
+    d, N, r = 128, 300, 32
+    X = rng.standard_normal((N, d)) * np.geomspace(1.0, 1e-3, d)
+    st = oracle.UnitState.empty(d, 64, r, N)
+    info = st.prefill_oneshot(X)
+    assert (st.n, st.e, st.k) == (N, 0, r)
+    C, sig, Bt = st.history()
+    S = np.linalg.svd(X, compute_uv=False)           # LAPACK, independent of the oracle's Jacobi
+    assert np.abs(sig - S[:r]).max() <= 1e-12 * S[0]
+    np.testing.assert_allclose(Bt @ Bt.T, np.eye(r), atol=1e-12)
+    np.testing.assert_allclose(C, X @ Bt.T, atol=1e-10 * S[0])   # C = X V_r = U_r Sigma_r
+    np.testing.assert_allclose(C.T @ C, np.diag(sig ** 2), atol=1e-9 * S[0] ** 2)
+    # Eckart-Young: the error is exactly the discarded energy
+    err2 = np.linalg.norm(X - C @ Bt) ** 2
+    assert abs(err2 - (S[r:] ** 2).sum()) <= 1e-9 * (S ** 2).sum()
+    assert abs(info.discarded - (S[r:] ** 2).sum()) <= 1e-9 * (S ** 2).sum()
+    # sign rule: each basis vector's entry of largest magnitude is positive
+    for j in range(r):
+        assert Bt[j, np.argmax(np.abs(Bt[j]))] > 0
+
+
+def test_oneshot_prefill_short_prompt_is_exact():
+    rng = np.random.default_rng(12)
+    d, N, r = 128, 40, 64
+    X = rng.standard_normal((N, d))
+    st = oracle.UnitState.empty(d, 64, r, N)
+    st.prefill_oneshot(X)
+    assert st.k == N                                  # k = min(r, n, d)
+    C, sig, Bt = st.history()
+    np.testing.assert_allclose(C @ Bt, X, atol=1e-11)
+    np.testing.assert_allclose(sig, np.linalg.svd(X, compute_uv=False), rtol=1e-12)
+
+
+def test_oneshot_prefill_then_folds_match_folding_everything():
+    """When nothing is truncated (r = d), a one-shot history followed by folds
+    reconstructs the same rows as folding every block: both are exact."""
+    rng = np.random.default_rng(13)
+    d, b, w, N, M = 128, 16, 8, 64, 100
+    X = rng.standard_normal((N + M, d))
+    a = oracle.UnitState.empty(d, b, d, N + M)
+    a.prefill_oneshot(X[:N])
+    a.append(X[N:], w)
+    np.testing.assert_allclose(a.reconstruct(), X, atol=1e-9)
