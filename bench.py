@@ -39,6 +39,9 @@ def parse():
                    help="event-time every n-th run of decode launches between two folds")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (default: one per core, <= 32)")
+    p.add_argument("--prefill", action="store_true",
+                   help="time the one-shot prompt factorisation of the long-input workload against "
+                        "folding the same prompt block by block, print one JSON line and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device-to-device copy and exit (reference for HBM byte counters)")
     return p.parse_args()
@@ -114,10 +117,76 @@ def cpu_baseline(w, nunits):
                           cores, dt)}
 
 
+def prefill_bench(args):
+    """Prompt compression of the long-input workload (65536 prompt rows per
+    unit, 32 layers x 8 kv heads, ranks 32 / 48): one iskv_prefill_oneshot
+    call against 1024 iskv_prefill_block calls over the same rows, both timed
+    with the inputs resident in HBM. Both leave the whole prompt in the
+    history (window empty)."""
+    import torch
+
+    import synth
+    from incremental_rank_svd_amd import iskv
+
+    w = synth.get_config("long_input_64k")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = iskv.load()
+    P = w.prefill_blocks * w.block
+    K = synth.kv_rows_torch(w, "K", P, dev)  # [B, L, Hk, P, d]
+    V = synth.kv_rows_torch(w, "V", P, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for mode in ("oneshot", "blocks"):
+        cache = iskv.Cache(iskv.config_from_workload(w), device=dev)
+        h = cache.h
+        blocks = [(K[:, :, :, s:s + w.block].contiguous(), V[:, :, :, s:s + w.block].contiguous())
+                  for s in range(0, P, w.block)] if mode == "blocks" else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if mode == "oneshot":
+            rc = lib.iskv_prefill_oneshot(h, ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()), P, 0,
+                                          w.layers, sp)
+            if rc:
+                raise RuntimeError("prefill_oneshot failed: %d" % rc)
+        else:
+            for kb, vb in blocks:
+                rc = lib.iskv_prefill_block(h, ctypes.c_void_p(kb.data_ptr()), ctypes.c_void_p(vb.data_ptr()), 0,
+                                            w.layers, sp)
+                if rc:
+                    raise RuntimeError("prefill_block failed: %d" % rc)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if cache.status():
+            raise RuntimeError("numeric flags %#x" % cache.status())
+        res[mode] = dt
+        del blocks, cache
+        torch.cuda.empty_cache()
+    rows = 2 * w.batch * w.layers * w.kv_heads * P
+    print(json.dumps({
+        "metric": "prompt KV rows factorised/sec",
+        "value": rows / res["oneshot"], "unit": "KV rows/s", "n_gpus": 1,
+        "ms": res["oneshot"] * 1e3, "higher_is_better": True,
+        "blockwise_ms": res["blocks"] * 1e3, "blockwise_value": rows / res["blocks"],
+        "speedup_vs_blockwise": res["blocks"] / res["oneshot"],
+        "dtype": "bf16 storage, f32 compute", "data": "synthetic (power-law spectrum KV, seeded), resident in HBM",
+        "config": {"workload": w.name, "batch": w.batch, "layers": w.layers, "kv_heads": w.kv_heads,
+                   "prompt_rows": P, "rank_k": w.rank_k, "rank_v": w.rank_v},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.prefill:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only; run with --gpus 1", file=sys.stderr)
+            sys.exit(2)
+        prefill_bench(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the compressed-cache path has no cross-GPU step "
