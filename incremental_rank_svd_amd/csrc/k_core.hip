@@ -894,7 +894,7 @@ __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
       Zb[(size_t)t * mz + D + i] = (r0 + i < a.nrows) ? ldf<TK>(src, (size_t)(r0 + i) * D + t) : 0.f;
     }
     __syncthreads();
-    house_qr<OS_M / 4, false>(Zb, mz, OS_M, D, D, tau);
+    house_qr<OS_M / 4, true>(Zb, mz, OS_M, D, D, tau);  // 256 = 4 x 64 rows: branch-free loads
     // keep R: clear the reflectors below its diagonal and the block rows
     for (int idx = tid; idx < D * OS_M; idx += NT) {
       const int col = idx / OS_M, row = idx - col * OS_M;
