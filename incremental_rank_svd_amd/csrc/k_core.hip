@@ -868,6 +868,71 @@ __host__ __device__ inline int oneshot_small() {  // float offset of tau, sv, sg
   return z > jh ? z : jh;
 }
 
+// One step of the blockwise QR: [R; X] -> [R'; 0], R upper triangular (D x
+// D, rows 0..D-1 of A) and X a block of D rows (rows D..2D-1), column-major
+// with column stride ld. Reflector j acts on row j and the block rows only:
+// the rows of R below its diagonal are zero and stay zero, so they are never
+// touched (half the work of a QR of the full 2D rows). Quad qid owns the
+// columns qid, qid + 64; lane q holds block rows D + q + 4e. The owner of
+// column j+1 builds reflector j+1 as soon as it has applied reflector j (one
+// barrier per reflector); the reflector's block part is kept in column j.
+__device__ __forceinline__ void tsqr_step(float *A, int ld, float *tau) {
+  constexpr int RQ = D / 4;
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  auto reflector = [&](int j) {
+    float *cj = A + (size_t)j * ld;
+    float x[RQ], sp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < RQ; e++) {
+      x[e] = cj[D + q + 4 * e];
+      sp[e & 3] += x[e] * x[e];
+    }
+    const float s = quad_sum((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    const float x0 = cj[j];
+    float tj = 0.f, beta = x0, scal = 0.f;
+    if (s > 0.f) {
+      beta = -copysignf(sqrtf(x0 * x0 + s), x0);
+      tj = (beta - x0) / beta;
+      scal = 1.f / (x0 - beta);
+    }
+#pragma unroll
+    for (int e = 0; e < RQ; e++) cj[D + q + 4 * e] = x[e] * scal;
+    if (q == 0) {
+      cj[j] = beta;
+      tau[j] = tj;
+    }
+  };
+  if (qid == 0) reflector(0);
+  __syncthreads();
+  for (int j = 0; j < D; j++) {
+    const float tj = tau[j];
+    if (tj != 0.f) {
+      const float *cj = A + (size_t)j * ld;
+      float v[RQ];
+#pragma unroll
+      for (int e = 0; e < RQ; e++) v[e] = cj[D + q + 4 * e];
+      int col = qid;
+      while (col <= j) col += NT / 4;
+      for (; col < D; col += NT / 4) {
+        float *cc = A + (size_t)col * ld;
+        float x[RQ], wp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < RQ; e++) {
+          x[e] = cc[D + q + 4 * e];
+          wp[e & 3] += v[e] * x[e];
+        }
+        const float rjc = cc[j];
+        const float w = tj * (rjc + quad_sum((wp[0] + wp[1]) + (wp[2] + wp[3])));
+#pragma unroll
+        for (int e = 0; e < RQ; e++) cc[D + q + 4 * e] = x[e] - w * v[e];
+        if (q == 0) cc[j] = rjc - w;
+      }
+    }
+    if (j + 1 < D && qid == ((j + 1) & (NT / 4 - 1))) reflector(j + 1);
+    __syncthreads();
+  }
+}
+
 template <typename TK, int XK>
 __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
   const Stream &X = a.X[XK];
@@ -894,13 +959,7 @@ __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
       Zb[(size_t)t * mz + D + i] = (r0 + i < a.nrows) ? ldf<TK>(src, (size_t)(r0 + i) * D + t) : 0.f;
     }
     __syncthreads();
-    house_qr<OS_M / 4, true>(Zb, mz, OS_M, D, D, tau);  // 256 = 4 x 64 rows: branch-free loads
-    // keep R: clear the reflectors below its diagonal and the block rows
-    for (int idx = tid; idx < D * OS_M; idx += NT) {
-      const int col = idx / OS_M, row = idx - col * OS_M;
-      if (row > col) Zb[(size_t)col * mz + row] = 0.f;
-    }
-    __syncthreads();
+    tsqr_step(Zb, mz, tau);  // R's rows below its diagonal stay zero; the block rows are reloaded
   }
   // R^T (R's rows as columns) into the Jacobi layout through registers, H = I
   const int c = D, sj = jac_stride(D), rl = jac_rl(D);
