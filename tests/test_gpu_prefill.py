@@ -137,3 +137,26 @@ def test_prefill_oneshot_rank_deficient_rows(iskv):
     ref = K[0, 0, 0, :200].double().cpu().numpy()
     assert np.linalg.norm(X - ref) <= 1e-5 * np.linalg.norm(ref)
     assert sig[3:k].max() <= 1e-5 * sig[0]
+
+
+def test_prefill_oneshot_layer_subset(iskv):
+    """One-shot prompt of layer 1 only (layer0 = 1 of 3, the input holding that
+    layer alone): layers 0 and 2 stay empty and then take block prefills."""
+    w = replace(synth.get_config(3), layers=3, kv_heads=2, q_heads=8, prefill_blocks=0, decode_tokens=600,
+                cfg_id=57)
+    rows = _rows(w, 512)
+    cache = iskv.Cache(iskv.config_from_workload(w, coord_dtype="f32"), device=DEV)
+    dt = tdtype(w.kv_dtype)
+    K = to_dev(rows["K"], dt, DEV)
+    V = to_dev(rows["V"], dt, DEV)
+    cache.prefill_oneshot(K[:, 1:2].contiguous(), V[:, 1:2].contiguous(), layer0=1)
+    assert cache.counts(0) == (0, 0, 0, 0) and cache.counts(2) == (0, 0, 0, 0)
+    assert cache.counts(1) == (512, 0, w.rank_k, w.rank_v)
+    for which, (x, r) in enumerate((("K", w.rank_k), ("V", w.rank_v))):
+        for h in range(w.kv_heads):
+            st = oracle.UnitState.empty(D, w.block, r, 600)
+            st.prefill_oneshot(rows[x][0, 1, h])
+            check_unit(cache, which, 0, 1, h, st, label=("layer subset", x, h))
+    cache.prefill_block(K[:, 0:1, :, :w.block].contiguous(), V[:, 0:1, :, :w.block].contiguous(), layer0=0)
+    assert cache.counts(0)[:2] == (w.block, 0) and cache.counts(1)[0] == 512 and cache.counts(2) == (0, 0, 0, 0)
+    assert cache.status() == 0
