@@ -357,6 +357,12 @@ int ora_fold(int d, int b, int r, int n, int k, double *C, int ldc, double *sigm
       }
       for (int jj = 0; jj < d; jj++) ci[jj] = (jj < kplus) ? tmp[jj] : 0.0;
     } else {
+#if defined(ORA_PLANT_NAIVE_SIGN)
+      for (int jj = 0; jj < kplus; jj++) ci[jj] *= sgn[jj];
+#elif defined(ORA_PLANT_NAIVE_PERM)
+      for (int jj = 0; jj < kplus; jj++) tmp[jj] = (perm[jj] < k) ? ci[perm[jj]] : 0.0;
+      for (int jj = 0; jj < kplus; jj++) ci[jj] = tmp[jj];
+#endif
       for (int jj = kplus; jj < d; jj++) ci[jj] = 0.0;
     }
   }
@@ -490,7 +496,16 @@ int ora_run(int d, int b, int r, int w, int N, int prefill, const double *X, int
   int first = 0;  /* index of the oldest unfolded row */
   ora_fold_info info;
   for (int s = 0; s < prefill; s += b) {
-    int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, X + (size_t)s * d, mode, 0, &info);
+#if defined(ORA_PLANT_PREFILL_REVERSED)
+    const double *Fs = X + (size_t)(prefill - b - s) * d;
+#else
+    const double *Fs = X + (size_t)s * d;
+#endif
+#if defined(ORA_PLANT_PREFILL_JOINT)
+    int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fs, 0, 0, &info);
+#else
+    int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fs, mode, 0, &info);
+#endif
     if (rc) return rc;
     if (log && folds < log_cap) {
       double *lg = log + (size_t)folds * 5;

@@ -30,6 +30,10 @@ PLANTS = [
     "ORA_PLANT_ATTEND_NOSCALE",
     "ORA_PLANT_RECON_WRONG_ROW",
     "ORA_PLANT_STORAGE_NO_SIGMA",
+    "ORA_PLANT_NAIVE_SIGN",
+    "ORA_PLANT_NAIVE_PERM",
+    "ORA_PLANT_PREFILL_REVERSED",
+    "ORA_PLANT_PREFILL_JOINT",
 ]
 
 

@@ -393,3 +393,108 @@ def test_oneshot_prefill_then_folds_match_folding_everything():
     a.prefill_oneshot(X[:N])
     a.append(X[N:], w)
     np.testing.assert_allclose(a.reconstruct(), X, atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# Fixed-coordinate update (section "The Basis Drift Problem": the basis moves,
+# the stored rows keep the coordinates they were written with)
+# --------------------------------------------------------------------------
+
+def _copy_state(st):
+    return oracle.UnitState(d=st.d, b=st.b, r=st.r, C=st.C.copy(), sigma=st.sigma.copy(),
+                            Bt=st.Bt.copy(), n=st.n, k=st.k)
+
+
+def test_fixed_coordinates_is_joint_fold_without_rewrite():
+    """From any state, a fold with fixed coordinates must equal a joint fold
+    from the same state in everything but the old rows, which keep their
+    previous values exactly (the rank never shrinks, so "cut or zero-padded
+    to k+" is the old columns followed by zeros). The chain continues in the
+    fixed-coordinate mode, so later states are ones the joint update never
+    reaches; the rank grows during the first folds (k+ > k) and then stays."""
+    X = _rows(0, "V", 64 * 9)
+    b, r = 64, 96
+    st = oracle.UnitState.empty(D, b, r, X.shape[0])
+    for t in range(9):
+        F = X[t * b:(t + 1) * b]
+        n, k = st.n, st.k
+        old = st.C[:n].copy()
+        ref = _copy_state(st)
+        ir = ref.fold(F, mode=0)
+        info = st.fold(F, mode=1)
+        assert (info.k, info.p, info.kplus) == (ir.k, ir.p, ir.kplus)
+        assert info.kplus >= k
+        assert abs(info.discarded - ir.discarded) <= 1e-12 * max(ir.discarded, 1e-300)
+        assert np.array_equal(st.Bt, ref.Bt) and np.array_equal(st.sigma, ref.sigma)
+        assert np.array_equal(st.C[n:n + b], ref.C[n:n + b])
+        assert np.array_equal(st.C[:n, :k], old[:, :k])
+        assert np.all(st.C[:n, k:] == 0)
+        if t >= 2:
+            # the joint fold rewrote the old rows; the fixed one did not
+            assert np.linalg.norm(ref.C[:n, :ir.kplus] - old[:, :ir.kplus]) > 1e-3 * np.linalg.norm(old)
+
+
+def test_fixed_coordinates_history_is_old_rows_in_new_basis():
+    """Plain definition of the drifting history: after a fixed-coordinate
+    fold, the reconstruction of an old row is its unchanged coordinates times
+    the NEW basis, so its error against the true row is measurable by hand."""
+    X = _rows(0, "K", 64 * 4)
+    b, r = 64, 128
+    st = oracle.UnitState.empty(D, b, r, X.shape[0])
+    st.fold(X[:b], mode=1)
+    C0 = st.C[:b, :st.k].copy()
+    st.fold(X[b:2 * b], mode=1)
+    rec = st.reconstruct()
+    np.testing.assert_allclose(rec[:b], C0 @ st.Bt[:C0.shape[1]], atol=1e-12)
+    # the first fold (untruncated) stored the rows exactly; the basis change moved them
+    assert np.linalg.norm(rec[:b] - X[:b]) > 1e-2 * np.linalg.norm(X[:b])
+    # the new block itself is exact (r = d: nothing truncated)
+    np.testing.assert_allclose(rec[b:2 * b], X[b:2 * b], atol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# Whole-stream driver with a prefill (section "Architecture Overview": the
+# exact window; prompt blocks fold straight into history)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prefill,N,w", [(128, 500, 64), (256, 256, 32), (64, 300, 0)])
+def test_run_with_prefill_untruncated_is_exact(prefill, N, w):
+    """With r = d nothing is truncated, so whatever the driver folds, history
+    plus window must reproduce every input row in order; the counts must
+    follow the window policy's closed form (synth.Workload.final_counts)."""
+    rng = np.random.default_rng(prefill + N)
+    X = rng.standard_normal((N, D)) * np.geomspace(1.0, 1e-2, D)
+    b = 64
+    st = oracle.run_unit(X, D, b, D, w, prefill=prefill)
+    from dataclasses import replace
+    wl = replace(synth.get_config(0), window=w, block=b, prefill_blocks=prefill // b,
+                 decode_tokens=N - prefill)
+    n, e, folds = wl.final_counts()
+    assert (st.n, st.e, len(st.log)) == (n, e, folds)
+    np.testing.assert_allclose(st.reconstruct(), X, atol=1e-10 * np.abs(X).max())
+    # rank sequence of the prefill folds: k = min(r, n, d) before each
+    for t in range(prefill // b):
+        assert st.log[t][0] == min(D, t * b)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_run_with_prefill_equals_explicit_folds(mode):
+    """The driver with a prefill equals the prompt folded block by block in
+    order, then the remaining rows through the window (truncating rank, every
+    update mode): same rank log, same stored history and window."""
+    X = _rows(0, "K", 700)
+    b, r, w, P = 64, 32, 64, 192
+    st = oracle.run_unit(X, D, b, r, w, prefill=P, mode=mode)
+    ref = oracle.UnitState.empty(D, b, r, X.shape[0])
+    for s in range(0, P, b):
+        ref.fold(X[s:s + b], mode=mode)
+    for t in range(P, X.shape[0]):
+        ref.window.append(X[t].copy())
+        if len(ref.window) >= w + b:
+            F = np.stack(ref.window[:b])
+            del ref.window[:b]
+            ref.fold(F, mode=mode)
+    assert (st.n, st.e, st.k) == (ref.n, ref.e, ref.k)
+    assert [l[:3] for l in st.log] == [l[:3] for l in ref.log]
+    np.testing.assert_allclose(st.reconstruct(), ref.reconstruct(), atol=1e-12 * np.abs(X).max())
+    np.testing.assert_allclose(st.sigma, ref.sigma, atol=1e-12 * ref.sigma[0])
