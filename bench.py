@@ -1,16 +1,27 @@
-"""Benchmark of the compressed-KV decode path on one MI355X.
+"""Benchmark of the compressed-KV path on one MI355X.
 
-One step = one whole decode run of the workload on synthetic inputs already
-resident in HBM: starting from an empty cache, every token appends one K and
-one V row to every layer (the window's oldest 64 rows fold into the low-rank
-history whenever it holds w + b rows) and then runs decode attention over the
-compressed cache of every layer, both through one iskv_append_decode call per
-token. For the Llama-3-8B-shaped workload that is 8192 tokens x 32 layers x
-8 kv heads, 126 fold rounds per unit stream.
+Default: the LLaMA-2-13B-shaped MHA workload (batch 16, 40 layers x 40 kv
+heads, b = 128, r_K = 64, r_V = 96, window 256, 16384 tokens), the largest
+workload that fits one GPU. Its history is injected before the timed region
+(each layer's first n0 rows factorised by iskv_prefill_oneshot, then the
+window filled to w rows), so that the timed steps are the last fold rounds of
+the 16384-token run. One step = the whole hot path over one batch of new
+rows: iskv_append_block of b new K and V rows per unit to all 40 layers
+(ingest, fold core, coordinate rewrite, commit: one fold round of 51200 unit
+streams), then iskv_decode_attn of one query per head over all 40 layers at
+the new n. Inputs (rows, queries) are resident in HBM before the timed region.
 
-Printed: one JSON line (metric, value = KV rows folded into history per
-second over the whole job, roofline of the dominant kernel measured with HIP
-events inside the timed region, CPU-oracle baseline).
+value = KV rows folded into history per second over the timed steps. Per
+kernel (core, rewrite, decode) durations come from HIP events on the launch
+stream inside the timed region (the library records caller events around the
+fold's kernels, iskv_set_fold_events); `roofline` is the kernel with the
+largest share of the step, `roofline_kernels` all three.
+
+--workload llama3_8b_gqa_8k --full-run: the whole Llama-3-8B-shaped decode run
+from an empty cache (one iskv_append_decode call per token, 8192 tokens).
+--prefill: one-shot prompt factorisation of the long-input workload.
+
+Printed: one JSON line.
 """
 
 import argparse
@@ -33,12 +44,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=3)
     p.add_argument("--warmup", type=int, default=1)
-    p.add_argument("--workload", default="llama3_8b_gqa_8k")
+    p.add_argument("--workload", default="llama2_13b_mha_16k")
+    p.add_argument("--full-run", action="store_true",
+                   help="time whole decode runs from an empty cache (one append_decode call per token)")
+    p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling runs only)")
     p.add_argument("--tokens", type=int, default=0, help="override decode tokens (profiling runs)")
     p.add_argument("--sample-every", type=int, default=1,
                    help="event-time every n-th run of decode launches between two folds")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (default: one per core, <= 32)")
+    p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (unit streams)")
     p.add_argument("--prefill", action="store_true",
                    help="time the one-shot prompt factorisation of the long-input workload against "
                         "folding the same prompt block by block, print one JSON line and exit")
@@ -117,6 +131,316 @@ def cpu_baseline(w, nunits):
                           cores, dt)}
 
 
+def core_flops(k, b, r, sweeps, d=128):
+    """Floating-point operations of one fold core for one unit stream, as the
+    kernel computes it: projection and residual (two passes), Householder QR
+    of [B | E^T] and the residual basis P, the QR of Z when it has more rows
+    than columns, `sweeps` one-sided Jacobi sweeps over c = k + p columns (one
+    fp64 dot product, two fp32 rotations of c-long columns per pair, column
+    norms per sweep), the basis update, the two Gram corrections and the new
+    rows. fp64 and fp32 operations are counted alike."""
+    p = min(b, d - k)
+    m, c = k + b, k + p
+    kp = min(r, c)
+    f = 8.0 * b * k * d
+    f += sum(4.0 * (d - j) * max(k + b - j, 0) for j in range(c))
+    f += sum(4.0 * (d - j) for col in range(p) for j in range(k + col + 1))
+    if m > c:
+        f += sum(4.0 * (m - j) * (c - j) for j in range(c))
+    f += sweeps * (c * (c - 1) / 2.0 * 14.0 * c + 2.0 * c * c)
+    f += 2.0 * d * c * kp + kp * kp * (2.0 * d + 2.0 * c) + 2.0 * kp * kp * d + 2.0 * c * kp * kp
+    f += 2.0 * b * c * kp
+    return f
+
+
+def rewrite_bytes(U, n, k, kp, coord_b):
+    """Algorithmic HBM bytes of one rewrite launch for one stream kind: the n
+    stored rows read (k columns) and written (k+ columns), H_top read."""
+    return U * (coord_b * (n * k + n * kp) + 4 * k * kp)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(cores or 1, 16))  # the GPU box's CPU share is 16 cores
+
+
+def cpu_baseline_fold_decode(w, n0, nunits):
+    """The fp64 oracle on a bounded sample of the same step: for each sampled
+    unit stream, a history of n0 + w rows (the same stage of the run as the
+    GPU's timed steps; its factorisation, taken with LAPACK, is setup and not
+    timed), then the oracle's fold of b new rows and its decode attention
+    (dense attention of one query over the reconstruction of history and
+    window). Units run in parallel threads on the host cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    oracle.load()
+    cores = host_cores()
+    if nunits <= 0:
+        nunits = 4 * cores
+    b, d = w.block, 128
+
+    def setup(i):
+        kind = "KV"[i % 2]
+        l, h = (i // 2) % w.layers, ((i // 2) * 7) % w.kv_heads
+        bb = ((i // 2) * 5) % w.batch
+        r = w.rank_k if kind == "K" else w.rank_v
+        X = synth.kv_rows(w, kind, bb, l, h, n0 + w.window + b)
+        u, sv, vt = np.linalg.svd(X[:n0], full_matrices=False)
+        st = oracle.UnitState.empty(d, b, r, n0 + w.window + 2 * b)
+        sg = np.sign(vt[np.arange(r), np.argmax(np.abs(vt[:r]), axis=1)])
+        st.C[:n0, :r] = u[:, :r] * sv[:r] * sg
+        st.sigma[:r] = sv[:r]
+        st.Bt[:r] = vt[:r] * sg[:, None]
+        st.n, st.k = n0, r
+        st.window = [x.copy() for x in X[n0:n0 + w.window]]
+        q = synth.queries(w, 0, bb, l)[h * w.group:(h + 1) * w.group]
+        return st, X[n0 + w.window:], q
+
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        jobs = list(ex.map(setup, range(nunits)))
+
+    def fold(j):
+        st, rows, _ = j
+        st.append(rows, w.window)
+        return st
+
+    def attend(j):
+        st, _, q = j
+        rec = st.reconstruct()
+        return oracle.attend(rec, rec, q, d ** -0.5)  # one stream's reconstruction stands for K and V
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        states = list(ex.map(fold, jobs))
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(attend, jobs))
+    t2 = time.perf_counter()
+    assert all(s.n == n0 + b for s in states)
+    rows_s = nunits * b / (t1 - t0)
+    # decode: each sampled stream is one of the 2 U streams a token's attention reads
+    U = w.units
+    tok_s = w.batch / ((t2 - t1) / nunits * 2 * U / cores)
+    return {"value": rows_s, "unit": "KV rows compressed/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "decode_attn_tokens_per_s": tok_s,
+            "sample": "%d unit streams of the %s workload (K and V alternating) at n = %d history rows "
+                      "plus a %d-row window: one fold of %d rows each (%.1f s wall), then dense attention "
+                      "of one query over the reconstruction (%.1f s wall); fp64 C oracle, %d threads; "
+                      "decode tokens/s scaled to the workload's %d streams per token" % (
+                          nunits, w.name, n0, w.window, b, t1 - t0, t2 - t1, cores, 2 * U)}
+
+
+def fold_decode_bench(args, w):
+    """One fold round plus one decode step per step, at the end of the run."""
+    import numpy as np
+    import torch
+
+    import synth
+    from incremental_rank_svd_amd import iskv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = iskv.load()
+    B, L, Hk, Hq, b, wnd = w.batch, w.layers, w.kv_heads, w.q_heads, w.block, w.window
+    U = B * L * Hk
+    kv_b = 2 if w.kv_dtype == "bf16" else 4
+    coord_b = 2 if w.coord_dtype == "bf16" else 4
+    kvdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    nsteps = args.warmup + args.steps
+    n_end = w.final_counts()[0]
+    n0 = n_end - nsteps * b
+    if n0 < b:
+        print("warmup + steps = %d fold rounds do not fit the %s run (at most %d)" % (
+            nsteps, w.name, n_end // b - 1), file=sys.stderr)
+        sys.exit(2)
+    cache = iskv.Cache(iskv.config_from_workload(w), device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    h = cache.h
+
+    # inputs: prompt rows per layer (factorised, then freed), window rows,
+    # and the rows of every step, resident in HBM
+    t_setup = time.perf_counter()
+    win = {x: torch.empty((B, L, Hk, wnd, 128), dtype=kvdt, device=dev) for x in "KV"}
+    steps_rows = {x: torch.empty((nsteps, B, L, Hk, b, 128), dtype=kvdt, device=dev) for x in "KV"}
+    for l in range(L):
+        rows = {x: synth.kv_rows_device(w, x, n0 + wnd + nsteps * b, dev, layer0=l, nlayers=1) for x in "KV"}
+        cache.prefill_oneshot(rows["K"][:, :, :, :n0].contiguous(), rows["V"][:, :, :, :n0].contiguous(),
+                              layer0=l)
+        for x in "KV":
+            win[x][:, l] = rows[x][:, 0, :, n0:n0 + wnd]
+            tail = rows[x][:, 0, :, n0 + wnd:].reshape(B, Hk, nsteps, b, 128)
+            steps_rows[x][:, :, l] = tail.permute(2, 0, 1, 3, 4)
+        del rows
+        if l % 8 == 7 or l == L - 1:
+            print("setup: %d of %d layers factorised (%.0f s)" % (l + 1, L, time.perf_counter() - t_setup),
+                  file=sys.stderr, flush=True)
+    for s0 in range(0, wnd, b):
+        s1 = min(wnd, s0 + b)
+        cache.append_block(win["K"][:, :, :, s0:s1].contiguous(), win["V"][:, :, :, s0:s1].contiguous())
+    del win
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.unit_key(w.cfg_id, 0, "Q", 0, 0, 0) & ((1 << 63) - 1))
+    Q = torch.randn((nsteps, B, L, Hq, 128), generator=gen, device=dev).to(kvdt)
+    out = torch.empty((B, L, Hq, 128), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    if cache.status():
+        raise RuntimeError("numeric flags %#x after the state injection" % cache.status())
+    n_start, e_start, kK, kV = cache.counts(0)
+    assert (n_start, e_start) == (n0, wnd), (n_start, e_start)
+    setup_s = time.perf_counter() - t_setup
+
+    VP = ctypes.c_void_p
+    scale = ctypes.c_float(128 ** -0.5)
+    kbytes = steps_rows["K"][0].numel() * steps_rows["K"].element_size()
+    qbytes = Q[0].numel() * Q.element_size()
+    kp0, vp0, qp0 = steps_rows["K"].data_ptr(), steps_rows["V"].data_ptr(), Q.data_ptr()
+    op = VP(out.data_ptr())
+
+    def events(k):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in evs:
+            e.record(stream)  # creates the underlying HIP event
+        return evs
+
+    step_evs = [events(6) for _ in range(nsteps)]  # ingest, core, rewrite, fold end, decode start, decode end
+    torch.cuda.synchronize()
+    sweeps_last = None
+
+    def run(s):
+        ev = step_evs[s]
+        arr = (VP * 4)(*[VP(e.cuda_event) for e in ev[:4]])
+        if lib.iskv_set_fold_events(h, arr):
+            raise RuntimeError("set_fold_events failed")
+        rc = lib.iskv_append_block(h, VP(kp0 + s * kbytes), VP(vp0 + s * kbytes), b, 0, L, sp)
+        if rc:
+            raise RuntimeError("append_block failed: %d" % rc)
+        ev[4].record(stream)
+        rc = lib.iskv_decode_attn(h, VP(qp0 + s * qbytes), op, 0, L, scale, sp)
+        if rc:
+            raise RuntimeError("decode_attn failed: %d" % rc)
+        ev[5].record(stream)
+
+    for s in range(args.warmup):
+        run(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, nsteps):
+        run(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.iskv_set_fold_events(h, None)
+    step_s = (t1 - t0) / args.steps
+    flags = cache.status()
+    if flags:
+        raise RuntimeError("numeric flags %#x" % flags)
+    n_fin, e_fin, kK, kV = cache.counts(0)
+    assert (n_fin, e_fin) == (n_end, wnd), (n_fin, e_fin)
+    sw = {x: cache.fold_stats(x)[0].double().mean().item() for x in (0, 1)}
+
+    # per-kernel durations (ms) over the timed steps
+    ms = {"ingest": [], "core": [], "rewrite": [], "decode": []}
+    for s in range(args.warmup, nsteps):
+        ev = step_evs[s]
+        ms["ingest"].append(ev[0].elapsed_time(ev[1]))
+        ms["core"].append(ev[1].elapsed_time(ev[2]))
+        ms["rewrite"].append(ev[2].elapsed_time(ev[3]))
+        ms["decode"].append(ev[4].elapsed_time(ev[5]))
+    avg = {k: float(np.mean(v)) for k, v in ms.items()}
+    # algorithmic work per launch, averaged over the timed steps (n grows by b per step)
+    core_f = rw_b = dec_b = 0.0
+    for s in range(args.warmup, nsteps):
+        n = n0 + s * b  # history rows before this step's fold
+        core_f += U * (core_flops(kK, b, w.rank_k, sw[0]) + core_flops(kV, b, w.rank_v, sw[1]))
+        rw_b += rewrite_bytes(U, n, kK, kK, coord_b) + rewrite_bytes(U, n, kV, kV, coord_b)
+        dec_b += decode_bytes(U, w.group, n + b, wnd, kK, kV, coord_b, kv_b)
+    core_f /= args.steps
+    rw_b /= args.steps
+    dec_b /= args.steps
+    kern = {
+        "k_core": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": 157.3,
+                   "unit": "TFLOP/s", "avg_launch_ms": avg["core"], "work_per_launch": core_f,
+                   "sweeps": [sw[0], sw[1]]},
+        "k_rewrite_mfma": {"bound": "hbm", "achieved": rw_b / (avg["rewrite"] * 1e-3) / 1e9,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_ms": avg["rewrite"],
+                           "work_per_launch": rw_b},
+        "k_decode_unit": {"bound": "hbm", "achieved": dec_b / (avg["decode"] * 1e-3) / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_ms": avg["decode"],
+                          "work_per_launch": dec_b},
+    }
+    traffic = measured_traffic(w.name)
+    for name, kr in kern.items():
+        kr["frac"] = kr["achieved"] / kr["peak"]
+        kr["share_of_step"] = kr["avg_launch_ms"] * 1e-3 / step_s
+        kr["traffic"] = traffic.get(name)
+    dom = max(kern, key=lambda k: kern[k]["share_of_step"])
+    rows_folded = 2 * U * b
+    res = {
+        "metric": METRIC,
+        "value": rows_folded / step_s,
+        "unit": "KV rows compressed/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 storage, f32 compute" if w.kv_dtype == "bf16" else "f32",
+        "data": "synthetic (power-law spectrum KV, seeded), resident in HBM",
+        "config": {"workload": w.name, "batch": B, "layers": L, "kv_heads": Hk, "q_heads": Hq,
+                   "head_dim": 128, "tokens": w.total_tokens, "block": b, "rank_k": w.rank_k,
+                   "rank_v": w.rank_v, "window": wnd,
+                   "step": "one fold round (b = %d new K and V rows per unit, all layers) + one decode "
+                           "query per head over all layers; history n = %d -> %d over the warmup and "
+                           "timed steps (the run's last fold rounds), window %d" % (b, n0, n_end, wnd)},
+        "decode_attn_tokens_per_s": B / (avg["decode"] * 1e-3),
+        "kernel_ms": avg,
+        "setup_s": setup_s,
+        "roofline": dict(kernel=dom, **{k: v for k, v in kern[dom].items()}),
+        "roofline_kernels": kern,
+    }
+    print("timed: %d steps, %.1f ms per step" % (args.steps, step_s * 1e3), file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_fold_decode(w, n0 + (args.warmup + args.steps // 2) * b,
+                                                       args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, per
+    kernel, while the kernel's source is unchanged since it was measured."""
+    tpath = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    out = {}
+    if not os.path.exists(tpath):
+        return out
+    try:
+        tr = json.load(open(tpath))
+        for name, ent in tr.get("kernels", {}).items():
+            src = os.path.join(ROOT, "incremental_rank_svd_amd", "csrc", ent["source"])
+            if ent.get("source_sha256_16") == source_hash(src):
+                out[name] = ent.get("bytes_per_launch")
+    except Exception:
+        return {}
+    return out
+
+
 def prefill_bench(args):
     """Prompt compression of the long-input workload (65536 prompt rows per
     unit, 32 layers x 8 kv heads, ranks 32 / 48): one iskv_prefill_oneshot
@@ -193,12 +517,25 @@ def main():
               "(units are independent); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import synth
+
+    w = synth.get_config(args.workload)
+    if args.layers:
+        from dataclasses import replace
+        w = replace(w, layers=args.layers)
+    if not args.full_run:
+        fold_decode_bench(args, w)
+        return
+    full_run_bench(args, w)
+
+
+def full_run_bench(args, w):
+    """Whole decode runs from an empty cache, one iskv_append_decode per token."""
     import torch
 
     import synth
     from incremental_rank_svd_amd import iskv
 
-    w = synth.get_config(args.workload)
     if args.tokens:
         from dataclasses import replace
         w = replace(w, decode_tokens=args.tokens)

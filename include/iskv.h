@@ -109,6 +109,16 @@ ISKV_API int iskv_reset(iskv_t h, void *stream);
  * with the next fold. */
 ISKV_API int iskv_set_mode(iskv_t h, int32_t mode);
 
+/* Timing hooks for profiling the fold. `events` is a host array of four
+ * hipEvent_t handles (passed as void*) created by the caller; from now on
+ * every fold enqueues hipEventRecord(events[0]) before its ingest copy,
+ * events[1] before the core kernel, events[2] before the coordinate rewrite
+ * and events[3] after it, on the call's stream (when a call folds several
+ * layer runs, the events of the last run remain). NULL turns the hooks off.
+ * The library neither creates nor destroys the events; they must stay valid
+ * while the hooks are on. ISKV_ERR_ARG if a handle is NULL. */
+ISKV_API int iskv_set_fold_events(iskv_t h, void *const *events);
+
 /* Append `nrows` (1..b) new K and V rows per sequence and kv head to layers
  * layer0 .. layer0+nlayers-1. k_rows, v_rows: [batch][nlayers][kv_heads][nrows][d]
  * in kv_dtype. Rows enter the exact window; when a layer's window then holds
@@ -124,8 +134,9 @@ ISKV_API int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows,
  * (section "Theoretical Foundation"); the window stays empty. k_rows,
  * v_rows: [batch][nlayers][kv_heads][nrows][d] in kv_dtype, device memory,
  * read only. Requires every such layer to be empty (n == 0 and e == 0, else
- * ISKV_ERR_STATE) and nrows <= max_tokens (else ISKV_ERR_CAPACITY). Later
- * appends fold into this history as usual. */
+ * ISKV_ERR_STATE) and nrows <= ncap = floor(max_tokens / b) * b, the history
+ * capacity in whole blocks (else ISKV_ERR_CAPACITY). nrows need not be a
+ * multiple of b. Later appends fold into this history as usual. */
 ISKV_API int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows,
                                   int32_t layer0, int32_t nlayers, void *stream);
 
@@ -137,7 +148,11 @@ ISKV_API int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows
                        int32_t nlayers, void *stream);
 
 /* Single-token decode attention over history factors plus the exact window
- * for layers layer0..layer0+nlayers-1: for every query head,
+ * for layers layer0..layer0+nlayers-1. Section "Reconstruction and Storage"
+ * defines the cached rows X~ (history rows U Sigma B^T, window rows exact);
+ * the output is softmax attention over X~, evaluated on the factors
+ * (C_K B_K^T q = C_K (B_K^T q) and p^T C_V B_V^T = (p^T C_V) B_V^T): for
+ * every query head,
  *   out = softmax(scale * [C_K (B_K^T q); K_win q]) applied to [C_V B_V^T; V_win].
  * q: [batch][nlayers][q_heads][d] in kv_dtype; out: same shape in fp32 (the
  * compute type; rounding it to bf16 would cost up to 2^-8 relative). Every
@@ -176,9 +191,12 @@ ISKV_API int iskv_counts(iskv_t h, int32_t layer, int32_t *n, int32_t *e, int32_
 ISKV_API int iskv_export_state(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head, void *C,
                       float *sigma, float *Bt, void *window, void *stream);
 
-/* Set a layer's counters (host), e.g. before importing a checkpoint.
- * Requires n % b == 0, k_k <= min(r_K, n, d), k_v <= min(r_V, n, d),
- * 0 <= e < w + b, n + e <= max_tokens. */
+/* Set a layer's counters (host), e.g. before importing a checkpoint (a
+ * state exported by iskv_export_state, or one a caller builds, such as a
+ * one-shot factorisation of any number of rows). Requires
+ * 0 <= n <= floor(max_tokens / b) * b, k_k <= min(r_K, n, d),
+ * k_v <= min(r_V, n, d), k > 0 exactly when n > 0, 0 <= e < w + b and
+ * n + e <= max_tokens; the window ring restarts at slot 0. */
 ISKV_API int iskv_set_counts(iskv_t h, int32_t layer, int32_t n, int32_t e, int32_t k_k, int32_t k_v);
 
 /* Copy one unit's state in (device to device), layouts as iskv_export_state,

@@ -21,6 +21,9 @@ struct iskv_ctx {
   std::vector<int> n, e, head, kk, kv;
   bool poisoned;
   int mode;  // ISKV_MODE_*
+  // caller's timing events recorded around each fold's kernels (see iskv_set_fold_events)
+  hipEvent_t fev[4];
+  bool fev_on;
 };
 
 static_assert(MODE_JOINT == ISKV_MODE_JOINT && MODE_FIXED_COORDS == ISKV_MODE_FIXED_COORDS &&
@@ -178,8 +181,10 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
     return ISKV_OK;
   }
   if (a.mode == ISKV_MODE_FIXED_BASIS) a.mode = ISKV_MODE_JOINT;  // first fold builds the basis
+  if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[1], s))) return ISKV_ERR_HIP;
   int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
   if (rc) return rc;
+  if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[2], s))) return ISKV_ERR_HIP;
   if (n > 0 && a.mode == ISKV_MODE_JOINT) {
     ra.u0 = u0;
     ra.n = n;
@@ -187,6 +192,7 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
     rc = fail_hip(h, launch_rewrite(ra, nunits, L.coord_bf16, s));
     if (rc) return rc;
   }
+  if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[3], s))) return ISKV_ERR_HIP;
   for (int l = l0; l < l1; l++) {
     h->n[l] += L.b;
     h->e[l] -= L.b;
@@ -254,6 +260,7 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *strea
   h->kv.assign(cfg->layers, 0);
   h->poisoned = false;
   h->mode = ISKV_MODE_JOINT;
+  h->fev_on = false;
   if (launch_zero(dev_ws, need, (hipStream_t)stream) != hipSuccess) {
     delete h;
     return ISKV_ERR_HIP;
@@ -267,6 +274,19 @@ int iskv_reset(iskv_t h, void *stream) {
   if (h->poisoned) return ISKV_ERR_POISONED;
   for (int l = 0; l < h->L.layers; l++) h->n[l] = h->e[l] = h->head[l] = h->kk[l] = h->kv[l] = 0;
   return fail_hip(h, launch_zero(h->L.status, 64, (hipStream_t)stream));
+}
+
+int iskv_set_fold_events(iskv_t h, void *const *events) {
+  if (!h) return ISKV_ERR_ARG;
+  if (!events) {
+    h->fev_on = false;
+    return ISKV_OK;
+  }
+  for (int i = 0; i < 4; i++)
+    if (!events[i]) return ISKV_ERR_ARG;
+  for (int i = 0; i < 4; i++) h->fev[i] = (hipEvent_t)events[i];
+  h->fev_on = true;
+  return ISKV_OK;
 }
 
 int iskv_set_mode(iskv_t h, int32_t mode) {
@@ -291,6 +311,8 @@ int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows, int32_t 
   hipStream_t s = (hipStream_t)stream;
   for (int l0 = layer0; l0 < layer0 + nlayers;) {
     const int l1 = run_end(h, l0, layer0 + nlayers);
+    if (h->fev_on && h->e[l0] + nrows >= w + b && fail_hip(h, hipEventRecord(h->fev[0], s)))
+      return ISKV_ERR_HIP;
     int rc = ingest_run(h, k_rows, v_rows, nrows, layer0, nlayers, l0, l1, s);
     if (rc) return rc;
     for (int l = l0; l < l1; l++) h->e[l] += nrows;
@@ -497,7 +519,7 @@ int iskv_set_counts(iskv_t h, int32_t layer, int32_t n, int32_t e, int32_t k_k, 
   if (h->poisoned) return ISKV_ERR_POISONED;
   const int b = h->L.b;
   auto kmax = [&](int r) { int m = r < n ? r : n; return m < D ? m : D; };
-  if (n < 0 || n % b != 0 || n > h->L.ncap || e < 0 || e >= h->L.w + b) return ISKV_ERR_ARG;
+  if (n < 0 || n > h->L.ncap || e < 0 || e >= h->L.w + b) return ISKV_ERR_ARG;
   if ((long long)n + e > h->cfg.max_tokens) return ISKV_ERR_CAPACITY;
   if (k_k < 0 || k_k > kmax(h->L.X[0].r) || k_v < 0 || k_v > kmax(h->L.X[1].r)) return ISKV_ERR_ARG;
   if ((n > 0) != (k_k > 0) || (n > 0) != (k_v > 0)) return ISKV_ERR_ARG;

@@ -1130,6 +1130,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     oneshot_svd_body<TK, 1>(a, smem);
 }
 
+// rows staged per pass of k_oneshot_coords: one thread per (row, column),
+// at most 64 rows (keeps the LDS of small ranks bounded)
+__host__ __device__ inline int oneshot_rows_per_pass(int r) { return NT / r < 64 ? NT / r : 64; }
+
 // C[i] = X_i B (kplus columns, zero to r) for every prompt row; sigma = the
 // column norms of the coordinates as stored. Rows are staged in LDS NT / r at
 // a time; thread (g, j) owns column j of row g of each pass.
@@ -1146,7 +1150,7 @@ __global__ void __launch_bounds__(NT) k_oneshot_coords(const OneshotArgs a) {
                   (((size_t)bi * a.nl_in + a.lrel0 + lrel) * a.kvh + hh) * (size_t)a.nrows * D;
   const int r = X.r;
   const int kplus = min(min(r, a.nrows), D);
-  const int G = NT / r;  // rows per pass
+  const int G = oneshot_rows_per_pass(r);  // rows per pass
   float *Bs = smem;                      // r x (D + 1)
   float *xs = Bs + (size_t)r * (D + 1);  // G x D
   float *part = xs + (size_t)G * D;      // G x r
@@ -1219,7 +1223,7 @@ hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coo
   if (e != hipSuccess) return e;
   const int rmin = a.X[0].r < a.X[1].r ? a.X[0].r : a.X[1].r;
   const int rmax = a.X[0].r > a.X[1].r ? a.X[0].r : a.X[1].r;
-  const size_t lds2 = sizeof(float) * ((size_t)rmax * (D + 1) + (size_t)(NT / rmin) * D + NT);
+  const size_t lds2 = sizeof(float) * ((size_t)rmax * (D + 1) + (size_t)oneshot_rows_per_pass(rmin) * D + NT);
   auto go = [&](const void *kf, auto kern) {
     hipError_t e2 = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
     if (e2 != hipSuccess) return e2;

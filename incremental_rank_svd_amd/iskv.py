@@ -36,6 +36,7 @@ EXPORTED = [
     "iskv_prefill_oneshot",
     "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
+    "iskv_set_fold_events",
 ]
 
 
@@ -70,6 +71,7 @@ def load(path: str = None):
     lib.iskv_init.argtypes = [ctypes.POINTER(Config), _vp, ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
     lib.iskv_reset.argtypes = [_vp, _vp]
     lib.iskv_set_mode.argtypes = [_vp, _i32]
+    lib.iskv_set_fold_events.argtypes = [_vp, ctypes.POINTER(_vp)]
     lib.iskv_append_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.iskv_prefill_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
     lib.iskv_decode_attn.argtypes = [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]

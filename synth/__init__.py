@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     bf16_round,
     haar_orthonormal,
     kv_rows,
+    kv_rows_device,
     kv_rows_torch,
     queries,
     round_to,

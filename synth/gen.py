@@ -118,3 +118,42 @@ def kv_rows_torch(cfg, kind: str, nrows: int, device, seed: int = 0, layers=None
             x = torch.matmul(g * s, w.transpose(1, 2).contiguous()) + cfg.noise * nz
             out[b, l] = x.to(tdt)
     return out
+
+
+def kv_rows_device(cfg, kind: str, nrows: int, device, layer0: int = 0, nlayers: int = 1, seed: int = 0):
+    """Throughput-run generator for large workloads: the same recipe as
+    kv_rows, computed on the device for the layers layer0 .. layer0+nlayers-1.
+
+    Returns [batch, nlayers, kv_heads, nrows, d] in the workload's kv dtype.
+    G and N come from torch's device generator (seeded per (batch, layer) from
+    the same key scheme); W is drawn per (layer, head) and shared by the
+    sequences of a batch, as a model's key/value subspaces are a property of
+    its layer and head; the product G diag(s) W^T is taken in bf16 with fp32
+    accumulation (the rows are stored in bf16 anyway). Values therefore differ
+    from kv_rows; the spectrum and shapes are the same.
+    """
+    import torch
+
+    d = cfg.head_dim
+    alpha = cfg.alpha_k if kind == "K" else cfg.alpha_v
+    tdt = torch.bfloat16 if cfg.kv_dtype == "bf16" else torch.float32
+    out = torch.empty((cfg.batch, nlayers, cfg.kv_heads, nrows, d), dtype=tdt, device=device)
+    s = torch.tensor(spectrum(d, alpha), dtype=torch.float32, device=device)
+    gen = torch.Generator(device=device)
+    for li in range(nlayers):
+        l = layer0 + li
+        a = np.stack([_gen(unit_key(cfg.cfg_id, seed, kind, 0, l, h, "W")).standard_normal((d, d))
+                      for h in range(cfg.kv_heads)])
+        q, r = np.linalg.qr(a)
+        q = q * np.sign(np.diagonal(r, axis1=1, axis2=2))[:, None, :]
+        wt = torch.tensor(np.ascontiguousarray(np.transpose(q, (0, 2, 1))), dtype=torch.float32,
+                          device=device).to(torch.bfloat16)  # [H, d, d] = W^T per head
+        for b in range(cfg.batch):
+            gen.manual_seed(unit_key(cfg.cfg_id, seed, kind, b, l, 0, "G") & ((1 << 63) - 1))
+            g = torch.randn((cfg.kv_heads, nrows, d), generator=gen, device=device)
+            x = torch.bmm((g * s).to(torch.bfloat16), wt).float()
+            del g
+            x += cfg.noise * torch.randn((cfg.kv_heads, nrows, d), generator=gen, device=device)
+            out[b, li] = x.to(tdt)
+            del x
+    return out

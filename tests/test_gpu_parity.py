@@ -140,34 +140,86 @@ def test_gqa_multi_unit(iskv, coord):
     note("  decode err %.2e" % derr)
 
 
-def test_rewrite_is_rotation_of_stored_rows(iskv):
-    """One fold rewrites every old row as C_old H_top with H_top = B_old^T B_new
-    (the basis change); bf16 rows within one bf16 ulp of the rounded product."""
+def _rotation_check(C0, B0, k0, n, C1, B1, k1):
+    """Old rows after a fold against C_old (B_old B_new^T) in fp64, which is
+    C_old H_top for any correct fold (B_new = [B_old P] H, B_old P = 0):
+    every value within one bf16 ulp of the rounded product for all but
+    1e-3 of them; returns the max deviation relative to the largest value."""
+    Ht = B0[:k0] @ B1[:k1].T  # k0 x k1
+    ref = C0[:n, :k0] @ Ht
+    ref_bf = synth.bf16_round(ref).astype(np.float64)
+    got = C1[:n, :k1]
+    _, ex = np.frexp(ref_bf)
+    ulp = np.ldexp(1.0, ex - 8)  # one bf16 ulp at each value
+    over = np.abs(got - ref_bf) > ulp * 1.0001
+    assert over.mean() <= 1e-3, over.mean()
+    assert np.all(C1[:n, k1:] == 0)
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+@pytest.mark.parametrize("shape", [
+    dict(rank_k=32, rank_v=32, block=64, window=128),    # K steps S = 1, column tiles T = 2
+    dict(rank_k=24, rank_v=48, block=64, window=128),    # ragged K step, T = 2 and 3
+    dict(rank_k=96, rank_v=64, block=64, window=64),     # the rank grows 64 -> 96 at the second fold
+    dict(rank_k=64, rank_v=96, block=128, window=256),   # the 13B-MHA shape: S = 2 and 3, T = 4 and 6
+])
+def test_rewrite_is_rotation_of_stored_rows(iskv, shape):
+    """Each of the second to fourth folds rewrites every old row as
+    C_old H_top (bf16 coordinates, matrix-core rewrite), including folds
+    where the rank grows (k+ > k)."""
     from dataclasses import replace
 
-    w = replace(synth.get_config(1), layers=2, kv_heads=4, q_heads=16, decode_tokens=600, cfg_id=12)
-    note("case: rewrite rotation")
+    b, wnd = shape["block"], shape["window"]
+    w = replace(synth.get_config(1), layers=2, kv_heads=4, q_heads=16, decode_tokens=wnd + 4 * b,
+                cfg_id=12 + shape["rank_k"], **shape)
+    note("case: rewrite rotation %s" % shape)
     rows = _rows_all(w, w.total_tokens)
     cache = _cache(iskv, w)
-    _feed(cache, w, rows, 0, 575, 64)
-    n0, e0, _, _ = cache.counts(0)
-    before = {(x, l, h): unit_state(cache, x, 0, l, h) for x in (0, 1) for l in range(2) for h in range(4)}
-    _feed(cache, w, rows, 575, 600, 25)  # triggers exactly one fold
-    n1, _, _, _ = cache.counts(0)
-    assert n1 == n0 + w.block
+    _feed(cache, w, rows, 0, wnd + b, b)  # first fold (empty history)
+    t = wnd + b
     worst = 0.0
-    for (x, l, h), (C0, s0, B0, _, n, _, k0) in before.items():
-        C1, s1, B1, _, n_, _, k1 = unit_state(cache, x, 0, l, h)
-        Ht = B0[:k0] @ B1[:k1].T  # k0 x k1
-        ref = C0[:n, :k0] @ Ht
-        ref_bf = synth.bf16_round(ref).astype(np.float64)
-        got = C1[:n, :k1]
-        _, ex = np.frexp(ref_bf)
-        ulp = np.ldexp(1.0, ex - 8)  # one bf16 ulp at each value
-        over = np.abs(got - ref_bf) > ulp * 1.0001
-        assert over.mean() <= 1e-3, (x, l, h, over.mean())
-        worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+    for fold in range(3):
+        _feed(cache, w, rows, t, t + b - 1, b)
+        t += b - 1
+        n0 = cache.counts(0)[0]
+        before = {(x, l, h): unit_state(cache, x, 0, l, h) for x in (0, 1) for l in range(2) for h in range(4)}
+        _feed(cache, w, rows, t, t + 1, 1)  # this row triggers exactly one fold
+        t += 1
+        assert cache.counts(0)[0] == n0 + b
+        for (x, l, h), (C0, s0, B0, _, n, _, k0) in before.items():
+            C1, s1, B1, _, n_, _, k1 = unit_state(cache, x, 0, l, h)
+            worst = max(worst, _rotation_check(C0, B0, k0, n, C1, B1, k1))
+    assert cache.status() == 0
     note("  max rel dev from fp64 rotation %.2e" % worst)
+
+
+def test_rewrite_long_history_all_rows(iskv):
+    """One fold over 40000 stored rows (more rows than one launch gives each
+    unit workgroups for, so the workgroups stride over the rows), ranks 24 and
+    48; then decode over the long history (matrix-core decode, r_K = 24,
+    r_V = 48)."""
+    from dataclasses import replace
+
+    n0 = 40000
+    w = replace(synth.get_config(1), layers=1, kv_heads=2, q_heads=8, rank_k=24, rank_v=48,
+                decode_tokens=n0 + 192, cfg_id=40)
+    note("case: rewrite over %d rows" % n0)
+    rows = _rows_all(w, w.total_tokens)
+    cache = _cache(iskv, w)
+    dt = tdtype(w.kv_dtype)
+    cache.prefill_oneshot(to_dev(rows["K"][:, :, :, :n0], dt, DEV), to_dev(rows["V"][:, :, :, :n0], dt, DEV))
+    before = {(x, h): unit_state(cache, x, 0, 0, h) for x in (0, 1) for h in range(2)}
+    _feed(cache, w, rows, n0, n0 + w.window + w.block, w.block)
+    assert cache.counts(0)[:2] == (n0 + w.block, w.window)
+    worst = 0.0
+    for (x, h), (C0, s0, B0, _, n, _, k0) in before.items():
+        C1, s1, B1, _, n_, _, k1 = unit_state(cache, x, 0, 0, h)
+        worst = max(worst, _rotation_check(C0, B0, k0, n, C1, B1, k1))
+    q = _queries(w, 2)
+    out = cache.decode_attn(to_dev(q, dt, DEV))
+    derr = _check_decode(cache, w, q, out, [(0, 0, 0), (0, 0, 1)])
+    assert cache.status() == 0
+    note("  max rel dev from fp64 rotation %.2e, decode err %.2e" % (worst, derr))
 
 
 @pytest.mark.parametrize("shape", [
@@ -359,7 +411,8 @@ def test_error_paths_leave_state_unchanged(iskv):
     assert cache.status() == 0
 
 
-@pytest.mark.parametrize("rk,rv,g,b", [(64, 96, 1, 128), (128, 8, 8, 64), (8, 128, 2, 64), (48, 24, 4, 64)])
+@pytest.mark.parametrize("rk,rv,g,b", [(64, 96, 1, 128), (128, 8, 8, 64), (8, 128, 2, 64), (48, 24, 4, 64),
+                                      (32, 48, 4, 64)])
 def test_bf16_decode_rank_and_group_shapes(iskv, rk, rv, g, b):
     """Matrix-core decode over several rank / GQA-group shapes, history long
     enough for several 1024-row blocks plus a ragged tail."""

@@ -2,6 +2,7 @@
 against the oracle's one-shot truncated SVD of the same rows, then ordinary
 appends folding into that history on both sides."""
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import replace
 
 import numpy as np
@@ -42,6 +43,7 @@ def _rows(w, ntok):
     (40, 64, 64, "f32"),     # fewer rows than d: k = nrows, exact
     (128, 128, 128, "f32"),  # untruncated, one full block
     (700, 32, 32, "bf16"),   # bf16 coordinates
+    (8192, 32, 48, "f32"),   # 64 QR blocks
 ])
 def test_prefill_oneshot_matches_oracle(iskv, nrows, rk, rv, coord):
     extra = 300
@@ -58,12 +60,19 @@ def test_prefill_oneshot_matches_oracle(iskv, nrows, rk, rv, coord):
     assert cache.counts(0) == (nrows, 0, min(rk, nrows, D), min(rv, nrows, D))
     assert cache.counts(1) == cache.counts(0)
     units = [(0, 0, 0), (0, 1, 1)]
-    states = {}
+    keys = [(which, b, l, h) for (b, l, h) in units for which in (0, 1)]
+
+    def one(key):
+        which, b, l, h = key
+        st = oracle.UnitState.empty(D, w.block, (rk, rv)[which], nrows + extra)
+        st.prefill_oneshot(rows["KV"[which]][b, l, h, :nrows])
+        return st
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        states = dict(zip(keys, ex.map(one, keys)))
     for (b, l, h) in units:
         for which, (x, r) in enumerate((("K", rk), ("V", rv))):
-            st = oracle.UnitState.empty(D, w.block, r, nrows + extra)
-            st.prefill_oneshot(rows[x][b, l, h, :nrows])
-            states[(which, b, l, h)] = st
+            st = states[(which, b, l, h)]
             if coord == "f32":
                 e1, e2, e3 = check_unit(cache, which, b, l, h, st, label=(nrows, x))
                 note("  %s sigma %.2e/%.2e recon %.2e" % (x, e1, e2, e3))
@@ -160,3 +169,44 @@ def test_prefill_oneshot_layer_subset(iskv):
     cache.prefill_block(K[:, 0:1, :, :w.block].contiguous(), V[:, 0:1, :, :w.block].contiguous(), layer0=0)
     assert cache.counts(0)[:2] == (w.block, 0) and cache.counts(1)[0] == 512 and cache.counts(2) == (0, 0, 0, 0)
     assert cache.status() == 0
+
+
+def test_prefill_oneshot_long_input_full_size(iskv):
+    """The long-input workload's prompt at full size: 65536 rows for each of
+    its 256 units (K and V), one iskv_prefill_oneshot call (the launch the
+    prefill benchmark times); sampled units against the oracle's one-shot
+    truncated SVD of the same rows (fp32 coordinates), the rest checked for
+    orthonormal bases."""
+    w = replace(synth.get_config(3), decode_tokens=0)
+    P = w.prefill_blocks * w.block
+    note("case: one-shot prefill of %d rows x %d units" % (P, w.units))
+    dev_rows = {x: synth.kv_rows_torch(w, x, P, DEV) for x in "KV"}
+    samples = [(0, 0, 0), (0, 31, 5)]
+    host = {}
+    for (b, l, h) in samples:
+        for x in "KV":
+            host[(x, b, l, h)] = synth.kv_rows(w, x, b, l, h, P)
+            dev_rows[x][b, l, h] = to_dev(host[(x, b, l, h)], torch.bfloat16, DEV)
+    cache = iskv.Cache(iskv.config_from_workload(w, coord_dtype="f32"), device=DEV)
+    cache.prefill_oneshot(dev_rows["K"], dev_rows["V"])
+    del dev_rows
+    assert cache.status() == 0
+    assert cache.counts(0) == (P, 0, w.rank_k, w.rank_v)
+    keys = [(which, b, l, h) for (b, l, h) in samples for which in (0, 1)]
+
+    def one(key):
+        which, b, l, h = key
+        st = oracle.UnitState.empty(D, w.block, (w.rank_k, w.rank_v)[which], P)
+        st.prefill_oneshot(host[("KV"[which], b, l, h)])
+        return st
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        states = dict(zip(keys, ex.map(one, keys)))
+    for (which, b, l, h), st in states.items():
+        e1, e2, e3 = check_unit(cache, which, b, l, h, st, label=("long input", which, b, l, h))
+        note("  %s %s sigma %.2e/%.2e recon %.2e" % ("KV"[which], (b, l, h), e1, e2, e3))
+    for (b, l, h) in [(0, 7, 3), (0, 20, 7)]:
+        for which in (0, 1):
+            C, sig, Bt, W, n, e, k = unit_state(cache, which, b, l, h)
+            assert np.abs(Bt[:k] @ Bt[:k].T - np.eye(k)).max() < 1e-5
+            assert np.all(np.diff(sig[:k]) <= 1e-6 * sig[0])

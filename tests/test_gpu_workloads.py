@@ -13,7 +13,6 @@ The long-input and 13B-MHA workloads keep their full per-unit sizes; the
 MHA one runs 2 of its 40 layers (units are independent).
 """
 
-import os
 from dataclasses import replace
 
 import numpy as np
@@ -27,11 +26,6 @@ from gpu_util import (D, DEC_TOL, check_unit, decode_err, decode_reference_on_gp
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-# The 32K-token, long-input and 13B-MHA cases take minutes of oracle time;
-# they run when ISKV_FULL_WORKLOADS=1 (their last results are summarised
-# under profiles/).
-heavy = pytest.mark.skipif(os.environ.get("ISKV_FULL_WORKLOADS") != "1",
-                           reason="set ISKV_FULL_WORKLOADS=1 to run the multi-minute workloads")
 
 
 @pytest.fixture(scope="module")
@@ -165,7 +159,6 @@ def test_llama3_8b_fp32_coordinates(iskv):
     _fp32_case(iskv, w, [(0, 0, 0), (0, 31, 7)])
 
 
-@heavy
 @pytest.mark.parametrize("coord", ["f32", "bf16"])
 def test_qwen3_8b_full(iskv, coord):
     w = synth.get_config(2)
@@ -174,7 +167,6 @@ def test_qwen3_8b_full(iskv, coord):
     (_fp32_case if coord == "f32" else _bf16_case)(iskv, w, samples)
 
 
-@heavy
 @pytest.mark.parametrize("coord", ["f32", "bf16"])
 def test_long_input_full(iskv, coord):
     w = synth.get_config(3)
@@ -183,7 +175,6 @@ def test_long_input_full(iskv, coord):
     (_fp32_case if coord == "f32" else _bf16_case)(iskv, w, samples)
 
 
-@heavy
 @pytest.mark.parametrize("coord", ["f32", "bf16"])
 def test_llama2_13b_mha_unit_sizes(iskv, coord):
     w = replace(synth.get_config(4), layers=2)
