@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libiskv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["iskv.hip", "k_core.hip", "k_rewrite.hip", "k_decode.hip", "k_misc.hip"]
+SOURCES = ["iskv.hip", "k_core.hip", "k_fold.hip", "k_rewrite.hip", "k_decode.hip", "k_misc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

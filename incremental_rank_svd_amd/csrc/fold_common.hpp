@@ -1,0 +1,283 @@
+// Device building blocks shared by the fold cores and the one-shot prefill:
+// LDS layouts, round-robin pair order, DPP lane-group sums, Householder QR
+// of an LDS-resident matrix, and one-sided Jacobi sweeps.
+//
+// Lane groups: a "quad" is 4 consecutive lanes, an "octet" 8. A quad or
+// octet owns one column (QR) or one Jacobi pair; its lanes split the rows in
+// contiguous chunks, and their partial sums are combined with DPP moves that
+// stay inside the group (no LDS traffic).
+#pragma once
+
+#include "iskv_internal.hpp"
+
+namespace iskv {
+namespace fold {
+
+constexpr int LDA = D + 4;  // LDS stride of 128-long rows (4 mod 32)
+__host__ __device__ inline int ldz(int m) { return ((m + 31) / 32) * 32 + 4; }
+
+// (column, row) of entry e of a column-major packed upper triangle
+__device__ __forceinline__ void tri_index(int e, int &col, int &row) {
+  int cc = (int)((sqrtf(8.f * (float)e + 1.f) - 1.f) * 0.5f);
+  while (cc > 0 && cc * (cc + 1) / 2 > e) cc--;
+  while ((cc + 1) * (cc + 2) / 2 <= e) cc++;
+  col = cc;
+  row = e - cc * (cc + 1) / 2;
+}
+
+// pair (i < j) of round `rnd` in a round-robin over c2 players (c2 even):
+// every pair meets exactly once in c2 - 1 rounds
+__device__ __forceinline__ void rr_pair(int rnd, int pr, int c2, int &i, int &j) {
+  int a, b;
+  if (pr == 0) {
+    a = rnd;
+    b = c2 - 1;
+  } else {
+    const int mdl = c2 - 1;
+    a = (rnd + pr) % mdl;
+    b = (rnd - pr + mdl) % mdl;
+  }
+  i = a < b ? a : b;
+  j = a < b ? b : a;
+}
+
+// DPP move of a double (two 32-bit moves with the same control)
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const int lo = (int)(u & 0xffffffffull), hi = (int)(u >> 32);
+  const int lo2 = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
+  const int hi2 = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi2 << 32) | (unsigned)lo2);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within each 8 lanes
+
+// Sum over the 4 lanes of a quad / the 8 lanes of an octet. Every lane ends
+// with the same value: a + b is computed as the same two operands on each.
+__device__ __forceinline__ double quad_sum_d(double v) {
+  v += dpp_d<DPP_QUAD_XOR1>(v);
+  v += dpp_d<DPP_QUAD_XOR2>(v);
+  return v;
+}
+__device__ __forceinline__ double octet_sum_d(double v) {
+  v = quad_sum_d(v);
+  // each lane of one quad meets a lane of the other quad of the octet
+  return v + dpp_d<DPP_ROW_HALF_MIRROR>(v);
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_QUAD_XOR1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_QUAD_XOR2, 0xF, 0xF, false));
+  return v;
+}
+template <int LP>
+__device__ __forceinline__ double group_sum_d(double v) {
+  static_assert(LP == 4 || LP == 8, "lane group of 4 or 8");
+  if constexpr (LP == 4) return quad_sum_d(v);
+  else return octet_sum_d(v);
+}
+
+// Householder QR (LAPACK dlarfg convention: H = I - tau v v^T, v[0] = 1,
+// H x = beta e_0) of an nrows x ncols matrix stored column-major in LDS with
+// column stride ld; nref reflectors. On return the upper triangle holds R,
+// the part below the diagonal v (without its unit head) and tau[j] the
+// scalars. Quad qid owns the columns qid, qid + NTC/4, ...; lane q of a quad
+// holds rows q, q+4, q+8, ... (RQ of them). The owner of column j+1 builds
+// reflector j+1 as soon as it has applied reflector j (one barrier per
+// reflector). ld should be 4 mod 32 so that the columns of different quads
+// start in different banks.
+template <int NTC, int RQ, bool FULL>
+__device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols, int nref, float *tau) {
+  // FULL: nrows == 4 RQ, so every row q + 4e exists. Then every load and
+  // store is unconditional (masking is arithmetic: v is zero above the
+  // diagonal, rows above it are written back unchanged), which lets a lane
+  // issue all RQ loads of a column back to back instead of one per branch.
+  constexpr int NQD = NTC / 4;
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  auto inrange = [&](int row) { return FULL || row < nrows; };
+  auto reflector = [&](int j) {
+    float *cj = A + (size_t)j * ld;
+    float s = 0.f;
+    float x[RQ];
+#pragma unroll
+    for (int e = 0; e < RQ; e++) {
+      const int row = q + 4 * e;
+      x[e] = 0.f;
+      if (FULL) {
+        x[e] = cj[row];
+      } else if (row < nrows) {
+        x[e] = cj[row];
+      }
+      const float t = (row > j && inrange(row)) ? x[e] : 0.f;
+      s += t * t;
+    }
+    s = quad_sum(s);
+    const float x0 = cj[j];
+    float tj = 0.f, beta = x0, scal = 0.f;
+    if (s > 0.f) {
+      beta = -copysignf(sqrtf(x0 * x0 + s), x0);
+      tj = (beta - x0) / beta;
+      scal = 1.f / (x0 - beta);
+    }
+#pragma unroll
+    for (int e = 0; e < RQ; e++) {
+      const int row = q + 4 * e;
+      if (FULL) {
+        cj[row] = (row > j) ? x[e] * scal : ((row == j) ? beta : x[e]);
+      } else {
+        if (row > j && row < nrows) cj[row] = x[e] * scal;
+        if (row == j) cj[j] = beta;
+      }
+    }
+    if (q == 0) tau[j] = tj;
+  };
+  if (nref > 0 && qid == 0) reflector(0);
+  __syncthreads();
+  for (int j = 0; j < nref; j++) {
+    const float tj = tau[j];
+    if (tj != 0.f) {
+      const float *cj = A + (size_t)j * ld;
+      float v[RQ];
+#pragma unroll
+      for (int e = 0; e < RQ; e++) {
+        const int row = q + 4 * e;
+        if (FULL) {
+          const float cv = cj[row];
+          v[e] = (row > j) ? cv : ((row == j) ? 1.f : 0.f);
+        } else {
+          v[e] = (row < nrows && row >= j) ? ((row == j) ? 1.f : cj[row]) : 0.f;
+        }
+      }
+      int col = qid;
+      while (col <= j) col += NQD;
+      for (; col < ncols; col += NQD) {
+        float *cc = A + (size_t)col * ld;
+        if (FULL) {
+          // column in registers: one pass of loads, one of stores
+          float x[RQ];
+          float w = 0.f;
+#pragma unroll
+          for (int e = 0; e < RQ; e++) {
+            x[e] = cc[q + 4 * e];
+            w += v[e] * x[e];
+          }
+          w = tj * quad_sum(w);
+#pragma unroll
+          for (int e = 0; e < RQ; e++) cc[q + 4 * e] = x[e] - w * v[e];
+        } else {
+          // two passes over the column (dot, then update): only v stays in registers
+          float w = 0.f;
+#pragma unroll
+          for (int e = 0; e < RQ; e++) {
+            const int row = q + 4 * e;
+            if (row < nrows && row >= j) w += v[e] * cc[row];
+          }
+          w = tj * quad_sum(w);
+#pragma unroll
+          for (int e = 0; e < RQ; e++) {
+            const int row = q + 4 * e;
+            if (row < nrows && row >= j) cc[row] -= w * v[e];
+          }
+        }
+      }
+    }
+    if (j + 1 < nref && qid == ((j + 1) & (NQD - 1))) reflector(j + 1);
+    __syncthreads();
+  }
+}
+
+// Cyclic sweeps of one-sided Jacobi over the c columns of J (column stride
+// sj; LP lanes per column pair, lane o holding the contiguous rows
+// o * 4NQ .. o * 4NQ + 4NQ - 1; rows past the column length are zero) without
+// accumulating the rotations: on convergence the columns are mutually
+// orthogonal (J V with V orthogonal). A lane group owns one pair of the
+// parallel round-robin order per round; cosines come from fp64 dot products.
+// The squared column norms (fp64, in nrm) are measured at the start of every
+// sweep and carried through each rotation by its exact effect on the two
+// norms, so a pair costs one dot product. A pair is rotated while its cosine
+// exceeds tol and neither column is negligible (squared norm <= negl:
+// rounding noise of the matrix). Stops after a sweep without rotation or at
+// SWEEP_CAP. (Taking the early sweeps' dot products in fp32 was tried: the
+// sweeps it adds cost more than it saves.)
+template <int NTC, int LP, int NQ>
+__device__ __forceinline__ void jacobi_columns(float *J, double *nrm, int sj, int c, double tol, double negl,
+                                               int &sweep, bool &conv) {
+  constexpr int NG = NTC / LP;  // lane groups
+  const int tid = threadIdx.x, o = tid % LP, gid = tid / LP;
+  const int c2 = c + (c & 1);
+  const int rl = 4 * NQ;
+  while (!conv && sweep < SWEEP_CAP) {
+    sweep++;
+    int rot = 0;
+    for (int col = gid; col < c; col += NG) {
+      const float4 *zc = (const float4 *)(J + (size_t)col * sj + o * rl);
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int e = 0; e < NQ; e++) {
+        const float4 x = zc[e];
+        s0 = fma((double)x.x, (double)x.x, s0);
+        s1 = fma((double)x.y, (double)x.y, s1);
+        s0 = fma((double)x.z, (double)x.z, s0);
+        s1 = fma((double)x.w, (double)x.w, s1);
+      }
+      const double sn2 = group_sum_d<LP>(s0 + s1);
+      if (o == 0) nrm[col] = sn2;
+    }
+    __syncthreads();
+    for (int rnd = 0; rnd < c2 - 1; rnd++) {
+      for (int pr = gid; pr < c2 / 2; pr += NG) {
+        int ci, cj;
+        rr_pair(rnd, pr, c2, ci, cj);
+        if (cj < c) {
+          float4 *zi = (float4 *)(J + (size_t)ci * sj + o * rl);
+          float4 *zj = (float4 *)(J + (size_t)cj * sj + o * rl);
+          float4 xi[NQ], xj[NQ];
+          const double al = nrm[ci], be = nrm[cj];
+          double ga = 0.0, ga2 = 0.0;
+#pragma unroll
+          for (int e = 0; e < NQ; e++) {
+            xi[e] = zi[e];
+            xj[e] = zj[e];
+          }
+#pragma unroll
+          for (int e = 0; e < NQ; e++) {
+            ga = fma((double)xi[e].x, (double)xj[e].x, ga);
+            ga2 = fma((double)xi[e].y, (double)xj[e].y, ga2);
+            ga = fma((double)xi[e].z, (double)xj[e].z, ga);
+            ga2 = fma((double)xi[e].w, (double)xj[e].w, ga2);
+          }
+          ga = group_sum_d<LP>(ga + ga2);
+          if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
+            // the sums are fp64; the angle only needs fp32 (it rotates fp32 columns)
+            const float zeta = (float)(be - al) / (float)(2.0 * ga);
+            const float az = fabsf(zeta);
+            float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
+            t = copysignf(t, zeta);
+            const float cs = 1.f / sqrtf(1.f + t * t);
+            const float sn = cs * t;
+#pragma unroll
+            for (int e = 0; e < NQ; e++) {
+              const float4 u0 = xi[e], u1 = xj[e];
+              zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                             cs * u0.w - sn * u1.w};
+              zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                             sn * u0.w + cs * u1.w};
+            }
+            if (o == 0) {
+              const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
+              nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
+              nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
+            }
+            rot = 1;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    conv = !__syncthreads_or(rot);
+  }
+}
+
+}  // namespace fold
+}  // namespace iskv

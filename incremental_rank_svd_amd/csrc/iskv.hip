@@ -182,7 +182,8 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
   }
   if (a.mode == ISKV_MODE_FIXED_BASIS) a.mode = ISKV_MODE_JOINT;  // first fold builds the basis
   if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[1], s))) return ISKV_ERR_HIP;
-  int rc = fail_hip(h, launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
+  int rc = fail_hip(h, a.mode == ISKV_MODE_JOINT ? launch_fold(a, nunits, L.kv_bf16, L.coord_bf16, s)
+                                                  : launch_core(a, nunits, L.kv_bf16, L.coord_bf16, s));
   if (rc) return rc;
   if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[2], s))) return ISKV_ERR_HIP;
   if (n > 0 && a.mode == ISKV_MODE_JOINT) {

@@ -71,7 +71,8 @@ struct FoldArgs {
   int pmax;          // rows of D floats per unit of the fold scratch (scratch_rows)
   uint32_t *status;
   int lds_small[2];  // float offset of the small arrays in dynamic LDS, per kind
-  int mode;          // ISKV_MODE_JOINT or ISKV_MODE_FIXED_COORDS (fixed basis: launch_project)
+  int mode;          // ISKV_MODE_JOINT (launch_fold) or ISKV_MODE_FIXED_COORDS (launch_core);
+                     // fixed basis: launch_project
 };
 
 struct RewriteArgs {
@@ -168,6 +169,9 @@ __device__ __forceinline__ float max64(float v) {
 // ---------------------------------------------------------------------------
 size_t core_lds_bytes(int k, int b, int r);
 hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);  // grid (nunits, 2)
+// joint-mode fold core (k_fold.hip): grid (nunits, 2), 512 threads per unit stream
+size_t fold_core_lds_bytes(int k, int b, int r);
+hipError_t launch_fold(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);  // K and V
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 // fixed-basis fold: new rows C[n + i] = F_i B (k columns), discarded energy

@@ -100,7 +100,7 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int RG = 2;  // 16-row groups in flight per wavefront
+constexpr int RG = 4;  // 16-row groups in flight per wavefront (each H fragment serves all of them)
 
 template <int XK>
 __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t *fr) {
@@ -156,24 +156,30 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
           cf[q][s] = *reinterpret_cast<const u32x4_t *>(C + (size_t)row * r + kb);
       }
     }
+    // each H fragment is read from LDS once for all RG groups
+    for (int t = 0; t < T; t++) {
+      f32x4_t acc[RG];
 #pragma unroll
-    for (int q = 0; q < RG; q++) {
-      const int row = (g0 + q * gstride) * 16 + (lane & 15);
-      for (int t = 0; t < T; t++) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < RG; q++) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-          if (s < S) {
-            const u32x4_t *fp = fr + (size_t)((t * S + s) * 3) * 64 + lane;
-            acc = mfma_bf16(fp[0], cf[q][s], acc);
-            acc = mfma_bf16(fp[64], cf[q][s], acc);
-            acc = mfma_bf16(fp[128], cf[q][s], acc);
+      for (int s = 0; s < 4; s++) {
+        if (s < S) {
+          const u32x4_t *fp = fr + (size_t)((t * S + s) * 3) * 64 + lane;
+#pragma unroll
+          for (int part = 0; part < 3; part++) {
+            const u32x4_t f = fp[64 * part];
+#pragma unroll
+            for (int q = 0; q < RG; q++) acc[q] = mfma_bf16(f, cf[q][s], acc[q]);
           }
         }
-        const int j0 = 16 * t + 4 * (lane >> 4);
+      }
+      const int j0 = 16 * t + 4 * (lane >> 4);
+#pragma unroll
+      for (int q = 0; q < RG; q++) {
+        const int row = (g0 + q * gstride) * 16 + (lane & 15);
         if (row < a.n && j0 < r) {
-          const uint32_t lo = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
-          const uint32_t hi = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+          const uint32_t lo = (uint32_t)f2bf(acc[q][0]) | ((uint32_t)f2bf(acc[q][1]) << 16);
+          const uint32_t hi = (uint32_t)f2bf(acc[q][2]) | ((uint32_t)f2bf(acc[q][3]) << 16);
           *reinterpret_cast<uint2 *>(C + (size_t)row * r + j0) = uint2{lo, hi};
         }
       }
@@ -199,8 +205,9 @@ hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipS
       const size_t l = (size_t)((a.r[x] + 15) / 16) * ((a.k[x] + 31) / 32) * 3 * 64 * 16;
       if (l > lds) lds = l;
     }
-    // about 512 rows per workgroup, at most 64 workgroups per unit
-    int tiles = (a.n + 511) / 512;
+    // about 2048 rows per workgroup (the H fragments are built once per
+    // workgroup), at most 64 workgroups per unit and kind
+    int tiles = (a.n + 2047) / 2048;
     if (tiles > 64) tiles = 64;
     hipError_t e = hipFuncSetAttribute((const void *)k_rewrite_mfma,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
