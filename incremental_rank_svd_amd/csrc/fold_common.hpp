@@ -203,10 +203,11 @@ __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols,
 template <int NTC, int LP, int NQ>
 __device__ __forceinline__ void jacobi_columns(float *J, double *nrm, int sj, int c, double tol, double negl,
                                                int &sweep, bool &conv) {
-  constexpr int NG = NTC / LP;  // lane groups
+  constexpr int NG = NTC / LP;  // lane groups; c <= 2 NG, so a group owns at most one pair per round
   const int tid = threadIdx.x, o = tid % LP, gid = tid / LP;
-  const int c2 = c + (c & 1);
+  const int c2 = c + (c & 1), mdl = c2 - 1;
   const int rl = 4 * NQ;
+  const bool has_pair = gid < c2 / 2;
   while (!conv && sweep < SWEEP_CAP) {
     sweep++;
     int rot = 0;
@@ -225,53 +226,62 @@ __device__ __forceinline__ void jacobi_columns(float *J, double *nrm, int sj, in
       if (o == 0) nrm[col] = sn2;
     }
     __syncthreads();
+    // round-robin players of this group's pair, advanced by one each round
+    // (the order of rr_pair without its two modulo operations per round)
+    int pa = gid == 0 ? 0 : gid, pb = gid == 0 ? c2 - 1 : mdl - gid;
     for (int rnd = 0; rnd < c2 - 1; rnd++) {
-      for (int pr = gid; pr < c2 / 2; pr += NG) {
-        int ci, cj;
-        rr_pair(rnd, pr, c2, ci, cj);
-        if (cj < c) {
-          float4 *zi = (float4 *)(J + (size_t)ci * sj + o * rl);
-          float4 *zj = (float4 *)(J + (size_t)cj * sj + o * rl);
-          float4 xi[NQ], xj[NQ];
-          const double al = nrm[ci], be = nrm[cj];
-          double ga = 0.0, ga2 = 0.0;
+      const int ci = pa < pb ? pa : pb, cj = pa < pb ? pb : pa;
+      if (has_pair && cj < c) {
+        float4 *zi = (float4 *)(J + (size_t)ci * sj + o * rl);
+        float4 *zj = (float4 *)(J + (size_t)cj * sj + o * rl);
+        float4 xi[NQ], xj[NQ];
+        const double al = nrm[ci], be = nrm[cj];
+        double g[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-          for (int e = 0; e < NQ; e++) {
-            xi[e] = zi[e];
-            xj[e] = zj[e];
-          }
-#pragma unroll
-          for (int e = 0; e < NQ; e++) {
-            ga = fma((double)xi[e].x, (double)xj[e].x, ga);
-            ga2 = fma((double)xi[e].y, (double)xj[e].y, ga2);
-            ga = fma((double)xi[e].z, (double)xj[e].z, ga);
-            ga2 = fma((double)xi[e].w, (double)xj[e].w, ga2);
-          }
-          ga = group_sum_d<LP>(ga + ga2);
-          if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
-            // the sums are fp64; the angle only needs fp32 (it rotates fp32 columns)
-            const float zeta = (float)(be - al) / (float)(2.0 * ga);
-            const float az = fabsf(zeta);
-            float t = (az > 1e18f) ? 0.5f / az : 1.f / (az + sqrtf(1.f + az * az));
-            t = copysignf(t, zeta);
-            const float cs = 1.f / sqrtf(1.f + t * t);
-            const float sn = cs * t;
-#pragma unroll
-            for (int e = 0; e < NQ; e++) {
-              const float4 u0 = xi[e], u1 = xj[e];
-              zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
-                             cs * u0.w - sn * u1.w};
-              zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
-                             sn * u0.w + cs * u1.w};
-            }
-            if (o == 0) {
-              const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
-              nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
-              nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
-            }
-            rot = 1;
-          }
+        for (int e = 0; e < NQ; e++) {
+          xi[e] = zi[e];
+          xj[e] = zj[e];
         }
+#pragma unroll
+        for (int e = 0; e < NQ; e++) {
+          g[0] = fma((double)xi[e].x, (double)xj[e].x, g[0]);
+          g[1] = fma((double)xi[e].y, (double)xj[e].y, g[1]);
+          g[2] = fma((double)xi[e].z, (double)xj[e].z, g[2]);
+          g[3] = fma((double)xi[e].w, (double)xj[e].w, g[3]);
+        }
+        const double ga = group_sum_d<LP>((g[0] + g[1]) + (g[2] + g[3]));
+        if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
+          // The rotation only has to be exact (cs^2 + sn^2 = 1 to rounding),
+          // not its angle: a slightly different angle leaves a cosine the next
+          // sweep removes. So the hardware reciprocal and reciprocal square
+          // root (about 1 ulp) take the place of correctly rounded ones.
+          const float zeta = (float)(be - al) * __builtin_amdgcn_rcpf((float)(2.0 * ga));
+          const float az = fabsf(zeta);
+          float t = __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.f)));
+          t = copysignf(t, zeta);
+          const float cs = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
+          const float sn = cs * t;
+#pragma unroll
+          for (int e = 0; e < NQ; e++) {
+            const float4 u0 = xi[e], u1 = xj[e];
+            zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
+                           cs * u0.w - sn * u1.w};
+            zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
+                           sn * u0.w + cs * u1.w};
+          }
+          if (o == 0) {
+            const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
+            nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
+            nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
+          }
+          rot = 1;
+        }
+      }
+      if (gid == 0) {
+        pa++;
+      } else {
+        pa = (pa + 1 == mdl) ? 0 : pa + 1;
+        pb = (pb + 1 == mdl) ? 0 : pb + 1;
       }
       __syncthreads();
     }

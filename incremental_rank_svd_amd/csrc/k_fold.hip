@@ -72,6 +72,87 @@ __device__ __forceinline__ void run_jacobi(float *J, double *nrm, int sj, int c,
   jacobi_columns<NTF, LPJ, NQ>(J, nrm, sj, c, tol, negl, sweep, conv);
 }
 
+// sum of a[e] * b[e] over N entries in four independent accumulation chains
+// (a dependent chain of N fmas is latency-bound)
+template <int N>
+__device__ __forceinline__ float dot_chains(const float *a, const float *b) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < N; e++) p[e & 3] = fmaf(a[e], b[e], p[e & 3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// Householder QR (LAPACK dlarfg convention: H = I - tau v v^T, v = 1 on row
+// j, H x = beta e_j) of ncol <= NTF / 4 columns of length D held in registers:
+// quad qid owns column qid, lane q rows 32q .. 32q + 31 (x). nref reflectors.
+// The owner of column j builds reflector j, stores v (zeros above row j, 1 on
+// it) in LDS row j of V (stride LDA; the rows must be free) and tau[j]; the
+// other quads apply it from LDS. The owner of column j + 1 builds reflector
+// j + 1 right after applying reflector j: one barrier per reflector. On
+// return quad col holds column col of R (zero below the diagonal for col <
+// nref) and V / tau define Q = H_0 ... H_{nref-1}.
+__device__ __forceinline__ void qr_columns_in_registers(float *V, float (&x)[D / 4], int ncol, int nref,
+                                                        float *tau) {
+  const int tid = threadIdx.x, q = tid & 3, qid = tid >> 2;
+  auto build = [&](int j) {
+    float xm[D / 4], x0 = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 4; e++) {
+      const int row = 32 * q + e;
+      xm[e] = (row > j) ? x[e] : 0.f;
+      x0 += (row == j) ? x[e] : 0.f;
+    }
+    const float s = quad_sum(dot_chains<D / 4>(xm, xm));
+    x0 = quad_sum(x0);
+    float tj = 0.f, beta = x0, scal = 0.f;
+    if (s != 0.f) {  // a non-finite column reaches R (and is flagged later) instead of being skipped
+      beta = -copysignf(sqrtf(x0 * x0 + s), x0);
+      tj = (beta - x0) / beta;
+      scal = 1.f / (x0 - beta);
+    }
+    float4 *vj = (float4 *)(V + (size_t)j * LDA + 32 * q);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      float t[4];
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        const int row = 32 * q + 4 * e + z;
+        t[z] = (row > j) ? x[4 * e + z] * scal : ((row == j) ? 1.f : 0.f);
+      }
+      vj[e] = float4{t[0], t[1], t[2], t[3]};
+    }
+#pragma unroll
+    for (int e = 0; e < D / 4; e++) {
+      const int row = 32 * q + e;
+      x[e] = (row == j) ? beta : ((row > j) ? 0.f : x[e]);
+    }
+    if (q == 0) tau[j] = tj;
+  };
+  if (nref > 0 && qid == 0) build(0);
+  __syncthreads();
+  for (int j = 0; j < nref; j++) {
+    const float tj = tau[j];
+    if (tj != 0.f && qid > j && qid < ncol) {
+      const float4 *vj = (const float4 *)(V + (size_t)j * LDA + 32 * q);
+      float v[D / 4];
+      float w = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float4 t = vj[e];
+        v[4 * e] = t.x;
+        v[4 * e + 1] = t.y;
+        v[4 * e + 2] = t.z;
+        v[4 * e + 3] = t.w;
+      }
+      w = tj * quad_sum(dot_chains<D / 4>(v, x));
+#pragma unroll
+      for (int e = 0; e < D / 4; e++) x[e] -= w * v[e];
+    }
+    if (j + 1 < nref && qid == j + 1) build(j + 1);
+    __syncthreads();
+  }
+}
+
 // R of Z = [diag(sigma) 0; Y] where Y (b x c) holds the block rows [F B | F P]:
 // one structured Householder step per column. Reflector j (LAPACK dlarfg
 // convention, H = I - tau v v^T with v = 1 on row j of R) touches only row j
@@ -94,10 +175,7 @@ __device__ __forceinline__ void tsqr_core(float *J, int sj, int c, int b, const 
     x[e] = (col < c && row < b) ? Y[(size_t)row * D + col] : 0.f;
   }
   auto build = [&](int j) {  // quad j: reflector j from R[j][j] and its block column
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < RB; e++) s += x[e] * x[e];
-    s = quad_sum(s);
+    const float s = quad_sum(dot_chains<RB>(x, x));
     const float x0 = J[(size_t)j * sj + j];
     float tj = 0.f, beta = x0, scal = 0.f;
     if (s != 0.f) {  // a non-finite block reaches R (and is flagged later) instead of being skipped
@@ -132,10 +210,8 @@ __device__ __forceinline__ void tsqr_core(float *J, int sj, int c, int b, const 
         v[4 * e + 2] = t.z;
         v[4 * e + 3] = t.w;
       }
-#pragma unroll
-      for (int e = 0; e < RB; e++) w += v[e] * x[e];
       const float rjc = J[(size_t)j * sj + col];
-      w = tj * (rjc + quad_sum(w));
+      w = tj * (rjc + quad_sum(dot_chains<RB>(v, x)));
 #pragma unroll
       for (int e = 0; e < RB; e++) x[e] -= w * v[e];
       if (q == 0) J[(size_t)j * sj + col] = rjc - w;
@@ -155,7 +231,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   const Stream &X = a.X[XK];
   const int b = a.b, k = a.k[XK], r = a.r[XK];
   const int p = (b < D - k) ? b : D - k;
-  const int m = k + b, c = k + p;
+  const int c = k + p;
   const int kplus = (r < c) ? r : c;
   const int sj = fold_sj(c);
   const FoldLds lay = fold_lds(k, b, r);
@@ -207,8 +283,13 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     }
   }
   __syncthreads();
+  // When k + b >= d the residual basis has p = d - k columns: it is any
+  // orthonormal basis of the complement of B (the residual rows lie in it),
+  // so it comes from the QR of B alone and E is not needed.
+  const bool cmpl = (k + b >= D);
+  const int nref = cmpl ? k : c;  // reflectors that define P
   // Y = F B and E = F - Y B^T; then once more E <- E - (E B) B^T
-  for (int pass = 0; pass < 2; pass++) {
+  for (int pass = 0; pass < (cmpl ? 1 : 2); pass++) {
     for (int j = 0; j < k; j++) {
       float bj[8];
 #pragma unroll
@@ -219,57 +300,102 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
 #pragma unroll
         for (int t = 0; t < 8; t++) s += f[qq][t] * bj[t];
         s = sum16(s);
+        if (!cmpl) {
 #pragma unroll
-        for (int t = 0; t < 8; t++) f[qq][t] -= s * bj[t];
+          for (int t = 0; t < 8; t++) f[qq][t] -= s * bj[t];
+        }
         const int i = grp + NGR * qq;
         if (pass == 0 && lane == 0 && i < b) YFP[i * D + j] = s;
       }
     }
   }
+  if (!cmpl) {
 #pragma unroll
-  for (int qq = 0; qq < NR; qq++) {
-    const int i = grp + NGR * qq;
-    if (i < b) {
+    for (int qq = 0; qq < NR; qq++) {
+      const int i = grp + NGR * qq;
+      if (i < b) {
 #pragma unroll
-      for (int t = 0; t < 8; t++) A[(k + i) * LDA + lane * 8 + t] = f[qq][t];
+        for (int t = 0; t < 8; t++) A[(k + i) * LDA + lane * 8 + t] = f[qq][t];
+      }
     }
   }
   __syncthreads();
 
   if (p > 0) {
-    // Householder QR of [B | E^T] (column j = LDS row j), c reflectors.
-    house_qr<NTF, D / 4, true>(A, LDA, D, k + b, c, tau);
-    // P = Q[:, k:k+p] = H_0 ... H_{c-1} [e_k .. e_{k+p-1}], accumulated backwards
-    // in the registers of one quad per column; reflectors j > k+col leave
-    // e_{k+col} unchanged and are skipped.
-    for (int col = qid; col < p; col += NTF / 4) {
-      float x[D / 4];
+    // Householder QR of [B | E^T] (column j = LDS row j), c reflectors; of B
+    // alone (k reflectors) when P is the complement of B. Each column lives in
+    // the registers of one quad (lane q: rows 32q .. 32q + 31); reflector j
+    // (v = 1 on row j, zero above) is stored in LDS row j once the columns are
+    // loaded.
+    const int ncol = cmpl ? k : k + b;  // <= 127 columns: one quad each
+    float x[D / 4];
+    if (qid < ncol) {
+      const float4 *src = (const float4 *)(A + (size_t)qid * LDA + 32 * q);
 #pragma unroll
-      for (int e = 0; e < D / 4; e++) x[e] = (q + 4 * e == k + col) ? 1.f : 0.f;
-      for (int j = k + col; j >= 0; j--) {
+      for (int e = 0; e < 8; e++) {
+        const float4 t = src[e];
+        x[4 * e] = t.x;
+        x[4 * e + 1] = t.y;
+        x[4 * e + 2] = t.z;
+        x[4 * e + 3] = t.w;
+      }
+    }
+    __syncthreads();  // LDS rows are free for the reflectors
+    qr_columns_in_registers(A, x, ncol, nref, tau);
+    if (!cmpl && qid >= k && qid < ncol) {
+      // F P = R[k:k+p, k:k+b]^T (lower trapezoidal): column k + i of R gives row i
+      const int i = qid - k;
+#pragma unroll
+      for (int e = 0; e < D / 4; e++) {
+        const int row = 32 * q + e;
+        if (row >= k && row < k + p) YFP[(size_t)i * D + row] = (row - k <= i) ? x[e] : 0.f;
+      }
+    }
+    // P = Q[:, k:k+p] = H_0 ... H_{nref-1} [e_k .. e_{k+p-1}], accumulated
+    // backwards in the registers of one quad per column; reflectors j > k+col
+    // leave e_{k+col} unchanged and are skipped.
+    for (int col = qid; col < p; col += NTF / 4) {
+#pragma unroll
+      for (int e = 0; e < D / 4; e++) x[e] = (32 * q + e == k + col) ? 1.f : 0.f;
+      for (int j = min(k + col, nref - 1); j >= 0; j--) {
         const float tj = tau[j];
         if (tj == 0.f) continue;
-        const float *cj = A + (size_t)j * LDA;
-        float vj[D / 4];
+        const float4 *vj = (const float4 *)(A + (size_t)j * LDA + 32 * q);
+        float v[D / 4];
         float w = 0.f;
 #pragma unroll
-        for (int e = 0; e < D / 4; e++) {
-          const int row = q + 4 * e;
-          const float cv = cj[row];
-          vj[e] = (row > j) ? cv : ((row == j) ? 1.f : 0.f);
-          w += vj[e] * x[e];
+        for (int e = 0; e < 8; e++) {
+          const float4 t = vj[e];
+          v[4 * e] = t.x;
+          v[4 * e + 1] = t.y;
+          v[4 * e + 2] = t.z;
+          v[4 * e + 3] = t.w;
         }
-        w = tj * quad_sum(w);
+        w = tj * quad_sum(dot_chains<D / 4>(v, x));
 #pragma unroll
-        for (int e = 0; e < D / 4; e++) x[e] -= w * vj[e];
+        for (int e = 0; e < D / 4; e++) x[e] -= w * v[e];
       }
+      float4 *dst = (float4 *)(Pg + (size_t)col * D + 32 * q);
 #pragma unroll
-      for (int e = 0; e < D / 4; e++) Pg[(size_t)col * D + q + 4 * e] = x[e];
+      for (int e = 0; e < 8; e++) dst[e] = float4{x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]};
     }
-    // F P = R[k:k+p, k:k+b]^T (lower trapezoidal)
-    for (int idx = tid; idx < b * p; idx += NTF) {
-      const int i = idx / p, qq = idx - i * p;
-      YFP[i * D + k + qq] = (qq <= i) ? A[(size_t)(k + i) * LDA + k + qq] : 0.f;
+    if (cmpl) {
+      // F P from the rows of F still in registers (16 lanes per row)
+      __syncthreads();  // P is complete
+      for (int col = 0; col < p; col++) {
+        float pv[8];
+#pragma unroll
+        for (int t = 0; t < 8; t++) pv[t] = Pg[(size_t)col * D + lane * 8 + t];
+#pragma unroll
+        for (int qq = 0; qq < NR; qq++) {
+          float s = 0.f;
+#pragma unroll
+          for (int t = 0; t < 8; t++) s += f[qq][t] * pv[t];
+          s = sum16(s);
+          const int i = grp + NGR * qq;
+          if (lane == 0 && i < b) YFP[i * D + k + col] = s;
+        }
+      }
     }
   }
   __syncthreads();

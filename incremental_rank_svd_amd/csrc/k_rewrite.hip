@@ -89,7 +89,9 @@ __global__ void __launch_bounds__(NT) k_rewrite_vec(const RewriteArgs a) {
 //   D: lane l holds output columns 4 (l / 16) .. +3 of row l % 16, stored as
 //       one 8-byte write.
 // H_top is fp32; it enters as three bf16 parts (hi + mid + lo, about 24 bits),
-// so the product is accurate to fp32 rounding before the bf16 store.
+// so the product is accurate to fp32 rounding before the bf16 store (with two
+// parts, values far below their row's norm can land more than one bf16 ulp
+// from the correctly rounded product).
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -101,6 +103,7 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 constexpr int RG = 4;  // 16-row groups in flight per wavefront (each H fragment serves all of them)
+constexpr int HP = 3;  // bf16 parts of H_top
 
 template <int XK>
 __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t *fr) {
@@ -134,9 +137,9 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
       w1[e / 2] = (uint32_t)p1[0] | ((uint32_t)p1[1] << 16);
       w2[e / 2] = (uint32_t)p2[0] | ((uint32_t)p2[1] << 16);
     }
-    fr[(f * 3 + 0) * 64 + lane] = u32x4_t{w0[0], w0[1], w0[2], w0[3]};
-    fr[(f * 3 + 1) * 64 + lane] = u32x4_t{w1[0], w1[1], w1[2], w1[3]};
-    fr[(f * 3 + 2) * 64 + lane] = u32x4_t{w2[0], w2[1], w2[2], w2[3]};
+    fr[(f * HP + 0) * 64 + lane] = u32x4_t{w0[0], w0[1], w0[2], w0[3]};
+    fr[(f * HP + 1) * 64 + lane] = u32x4_t{w1[0], w1[1], w1[2], w1[3]};
+    fr[(f * HP + 2) * 64 + lane] = u32x4_t{w2[0], w2[1], w2[2], w2[3]};
   }
   __syncthreads();
   uint16_t *C = (uint16_t *)X.C + (size_t)u * X.cstride;
@@ -164,9 +167,9 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
 #pragma unroll
       for (int s = 0; s < 4; s++) {
         if (s < S) {
-          const u32x4_t *fp = fr + (size_t)((t * S + s) * 3) * 64 + lane;
+          const u32x4_t *fp = fr + (size_t)((t * S + s) * HP) * 64 + lane;
 #pragma unroll
-          for (int part = 0; part < 3; part++) {
+          for (int part = 0; part < HP; part++) {
             const u32x4_t f = fp[64 * part];
 #pragma unroll
             for (int q = 0; q < RG; q++) acc[q] = mfma_bf16(f, cf[q][s], acc[q]);
@@ -202,7 +205,7 @@ hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipS
   if (coord_bf16 && a.r[0] % 8 == 0 && a.r[1] % 8 == 0) {
     size_t lds = 0;
     for (int x = 0; x < 2; x++) {
-      const size_t l = (size_t)((a.r[x] + 15) / 16) * ((a.k[x] + 31) / 32) * 3 * 64 * 16;
+      const size_t l = (size_t)((a.r[x] + 15) / 16) * ((a.k[x] + 31) / 32) * HP * 64 * 16;
       if (l > lds) lds = l;
     }
     // about 2048 rows per workgroup (the H fragments are built once per
