@@ -416,11 +416,41 @@ def fold_decode_bench(args, w):
         "roofline": dict(kernel=dom, **{k: v for k, v in kern[dom].items()}),
         "roofline_kernels": kern,
     }
+    # decode of one layer per call, as a model's layer loop issues it (after the timed region)
+    res["decode_one_layer"] = one_layer_decode(lib, h, Q[-1], out, L, B, Hk, Hq, n_fin, wnd, kK, kV, w.group,
+                                               coord_b, kv_b, stream, sp)
     print("timed: %d steps, %.1f ms per step" % (args.steps, step_s * 1e3), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_fold_decode(w, n0 + (args.warmup + args.steps // 2) * b,
                                                        args.cpu_units)
     print(json.dumps(res), flush=True)
+
+
+def one_layer_decode(lib, h, q, out, L, B, Hk, Hq, n, e, kK, kV, g, coord_b, kv_b, stream, sp, reps=50):
+    """Median latency of iskv_decode_attn over a single layer (layer 0), the
+    call a model's per-layer decode loop makes: B * Hk units, history split
+    over several workgroups per unit. q, out: [B, L, Hq, 128] (one layer
+    slice is passed)."""
+    import torch
+
+    VP = ctypes.c_void_p
+    q1 = q[:, :1].contiguous()
+    o1 = out[:, :1].contiguous()
+    scale = ctypes.c_float(128 ** -0.5)
+    evs = []
+    for _ in range(reps):
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        if lib.iskv_decode_attn(h, VP(q1.data_ptr()), VP(o1.data_ptr()), 0, 1, scale, sp):
+            raise RuntimeError("decode_attn (one layer) failed")
+        a1.record(stream)
+        evs.append((a0, a1))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1e3
+    U1 = B * Hk
+    byts = decode_bytes(U1, g, n, e, kK, kV, coord_b, kv_b)
+    return {"units": U1, "n": n, "median_us_with_event_pair": us, "GBps": byts / (us * 1e-6) / 1e9}
 
 
 def measured_traffic(workload):
@@ -702,6 +732,8 @@ def full_run_bench(args, w):
                      "avg_launch_us": dec_avg_us, "launches_sampled": dec_launches,
                      "share_of_step": dec_share},
     }
+    res["decode_one_layer"] = one_layer_decode(lib, h, Q[-1], out, L, B, Hk, Hq, n, e, kK, kV, w.group,
+                                               coord_b, kv_b, stream, sp)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
     print(json.dumps(res), flush=True)

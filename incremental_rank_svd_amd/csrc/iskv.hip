@@ -99,6 +99,12 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
     s.sweeps = (int32_t *)take(U * 4);
     s.disc = (float *)take(U * 4);
   }
+  // split decode partials: launches over at most split_units units, at most
+  // split_max workgroups per unit (each split takes >= 1024 history rows)
+  l.split_units = (int)(U < 128 ? U : 128);
+  l.split_max = l.ncap / 1024 < 64 ? l.ncap / 1024 : 64;
+  if (l.split_max < 1) l.split_max = 1;
+  l.spart = (float *)take((size_t)l.split_units * l.split_max * decode_split_floats(l.g, c->rank_v) * 4);
   l.ticket = (uint32_t *)take(U * 4);
   l.part = (float *)take(U * l.nchunk_max * l.g * (2 + c->rank_v) * 4);
   l.wpart = (float *)take(U * l.g * (2 + D) * 4);
@@ -389,6 +395,29 @@ int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32
   return ISKV_OK;
 }
 
+// Split the history of each unit over several workgroups when a launch has
+// too few units to fill the chip (e.g. one layer per call): at most smax
+// splits of >= 1024 rows (multiples of 32), about 512 workgroups in all.
+static void choose_split(DecodeArgs &a, int nunits, int smax, float *spart, bool force) {
+  a.nsplit = 0;
+  if (!decode_can_split(a)) return;
+  int ns = 1;
+  if (2 * nunits <= 256 && a.n >= 2048) {
+    ns = (512 + nunits - 1) / nunits;
+    if (ns > smax) ns = smax;
+    if (ns > a.n / 1024) ns = a.n / 1024;
+    if (ns < 1) ns = 1;
+  }
+  if (ns < 2 && !force) return;
+  int rows = (a.n + ns - 1) / ns;
+  rows = ((rows + 31) / 32) * 32;
+  if (rows < 32) rows = 32;
+  a.split_rows = rows;
+  a.nsplit = (a.n + rows - 1) / rows;
+  if (a.nsplit < 1) a.nsplit = 1;
+  a.spart = spart;
+}
+
 static DecodeArgs decode_args(iskv_t h, const void *q, float *out, int layer0, int nlayers, int l0, int l1,
                               float scale) {
   DecodeArgs a = {};
@@ -407,6 +436,8 @@ static DecodeArgs decode_args(iskv_t h, const void *q, float *out, int layer0, i
   const int chunk = decode_chunk_rows(h->L);
   a.nchunk = (a.n + chunk - 1) / chunk;
   a.scale = scale;
+  const int nunits = h->L.batch * (l1 - l0) * h->L.kvh;
+  if (nunits <= h->L.split_units) choose_split(a, nunits, h->L.split_max, h->L.spart, false);
   return a;
 }
 
@@ -461,6 +492,7 @@ int iskv_append_decode(iskv_t h, const void *k_rows, const void *v_rows, const v
     a.nk = k_rows;
     a.nv = v_rows;
     a.nnew = 1;
+    a.nsplit = 0;  // the fused append runs one workgroup per unit
     const int rc = fail_hip(h, launch_decode(a, s));
     if (rc) return rc;
     for (int l = l0; l < l1; l++) h->e[l] += 1;

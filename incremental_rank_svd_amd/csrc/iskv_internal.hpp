@@ -58,6 +58,9 @@ struct Layout {
   float *wpart;   // [U][g][2 + D] window part (max, sum, o)
   int chunk;      // history rows per decode chunk
   int nchunk_max;
+  // split decode partials of launches over at most split_units units
+  float *spart;
+  int split_units, split_max;
 };
 
 // One fold round: both stream kinds in one launch (blockIdx.y = 0 keys, 1 values).
@@ -101,6 +104,10 @@ struct DecodeArgs {
   // written to the ring at position e and attended as window row e
   const void *nk, *nv;
   int nnew;
+  // split history (bf16 matrix-core path, nnew == 0): nsplit > 0 workgroups per
+  // unit of split_rows rows each, partials [units][nsplit][g][2 + r_V + D] in spart
+  int nsplit, split_rows;
+  float *spart;
 };
 
 // One-shot prefill of a layer run: every unit's nrows prompt rows
@@ -181,6 +188,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 // true when launch_decode can take the appended row itself (nnew = 1)
 bool decode_can_fuse(const DecodeArgs &a);
+// true when the split (matrix-core) decode applies to these counters
+bool decode_can_split(const DecodeArgs &a);
+// floats of split partials per unit and split
+inline size_t decode_split_floats(int g, int rank_v) { return (size_t)g * (2 + rank_v + D); }
 int decode_chunk_rows(const Layout &L);  // history rows per decode block
 hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, int e, int head,
                               float *out, hipStream_t s);

@@ -565,17 +565,22 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u3
   }
 }
 
-template <int KS, int NTV>
+// SPLIT: grid (units, nsplit); workgroup s takes history rows
+// [s split_rows, (s + 1) split_rows) and workgroup 0 also the window; each
+// leaves its partial (max, sum, o', window values) per query head in
+// a.spart for k_decode_merge instead of writing the output.
+template <int KS, int NTV, bool SPLIT>
 __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   extern __shared__ float sm[];
   const int ul = blockIdx.x, u = a.u0 + ul;
   const int g = a.L.g, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rsK = a.L.X[0].r, rsV = a.L.X[1].r;
+  const bool hasw = !SPLIT || blockIdx.y == 0;  // this workgroup attends the window
   float *qsm = sm;                                          // g x rsK: q'
   u32x4_t *frag = (u32x4_t *)(qsm + (size_t)MAXG * rsK);    // [(kc*2 + part)*64 + lane]
   u32x4_t *qfrag = frag + 4 * 2 * 64;                        // [kc*64 + lane]: q itself (bf16)
   float *big = qsm + decode_unit_qs(rsK);                   // tiles, then combine scratch
-  const int nwo = decode_unit_nwo(a.wlds ? a.e + a.nnew : 0);
+  const int nwo = hasw ? decode_unit_nwo(a.wlds ? a.e + a.nnew : 0) : 0;
   uint16_t *wsm = (uint16_t *)(big + decode_unit_big(rsV, g, nwo));  // [2][e][WSTR] window copy
   int li, bi, h;
   unit_coords(a, ul, li, bi, h);
@@ -585,7 +590,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   // The window rows are copied to LDS in batches of WB 16-byte chunks per
   // thread; the first batch's loads are in flight during the q' projection.
   constexpr int WB = 8;
-  const int ew = a.e + a.nnew;                      // window rows, the appended one last
+  const int ew = hasw ? a.e + a.nnew : 0;          // window rows, the appended one last
   const int wch = a.wlds ? 2 * ew * (D / 8) : 0;  // K rows, then V rows
   const size_t nrow_off = (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.kvh + h) * D;
   u32x4_t wbuf[WB];
@@ -622,10 +627,12 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   };
   if (wch > 0) win_load(0);
   // this wave's history slice; its first step is loaded before the projection
-  int per = (a.n + NWU - 1) / NWU;
+  const int h0 = SPLIT ? blockIdx.y * a.split_rows : 0;
+  const int h1 = SPLIT ? min(a.n, h0 + a.split_rows) : a.n;
+  int per = (max(h1 - h0, 0) + NWU - 1) / NWU;
   per = ((per + 31) / 32) * 32;
-  const int wb = wv * per;
-  const int we = min(a.n, wb + per);
+  const int wb = h0 + wv * per;
+  const int we = min(h1, wb + per);
   const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride;
   const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
   // prefetching the next step doubles the load registers: only when they fit
@@ -801,10 +808,12 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       }
   }
   // ---- window rows: row i goes to lane group (i mod 64) of the workgroup ----
-  if (a.wlds)
-    window_mfma(a, ew, qfrag, wsm, wsm + (size_t)ew * WSTR, wo, g, wv, lane);
-  else
-    window_part(a, q, kr, vr, wo, g, wv, lane);
+  if (hasw) {
+    if (a.wlds)
+      window_mfma(a, ew, qfrag, wsm, wsm + (size_t)ew * WSTR, wo, g, wv, lane);
+    else
+      window_part(a, q, kr, vr, wo, g, wv, lane);
+  }
   __syncthreads();
   // ---- combine all waves: per head the max, the sum, o' and window values ---
   if (tid < g) {
@@ -840,6 +849,26 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     ow[idx] = s;
   }
   __syncthreads();
+  if constexpr (SPLIT) {
+    // partial of this workgroup: (max, sum, o', window values) per head
+    const int rs = 2 + rsV + D;
+    float *rec = a.spart + ((size_t)ul * gridDim.y + blockIdx.y) * g * rs;
+    for (int idx = tid; idx < g * rs; idx += NTU) {
+      const int hh = idx / rs, t = idx - hh * rs;
+      const float L = fac[hh * 8 + 1];
+      float v;
+      if (t == 0)
+        v = (L > 0.f) ? fac[hh * 8] : -INFINITY;
+      else if (t == 1)
+        v = L;
+      else if (t < 2 + rsV)
+        v = op[hh * rsV + t - 2];
+      else
+        v = ow[hh * D + t - 2 - rsV];
+      rec[idx] = v;
+    }
+    return;
+  }
   float *out = (float *)a.out + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
   if (bv_early) {
     const int hh = ot / D;
@@ -863,6 +892,58 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   }
 }
 
+// Log-sum-exp merge of the split partials of k_decode_unit<..., true>: per
+// query head M = max_s m_s, L = sum_s l_s e^(m_s - M), then
+// out = (sum_s e^(m_s - M) w_s + (sum_s e^(m_s - M) o'_s) B_V^T) / L, with w_s
+// the window values (workgroup 0 only) and o'_s the weighted coordinates.
+__global__ void __launch_bounds__(NT) k_decode_merge(const DecodeArgs a) {
+  __shared__ float fac[MAXG][2];
+  __shared__ float op[MAXG][D];  // merged o' (rsV <= D entries per head)
+  __shared__ float ow[MAXG][D];  // merged window values
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int g = a.L.g, rsV = a.L.X[1].r, tid = threadIdx.x;
+  const int rs = 2 + rsV + D, ns = a.nsplit;
+  const float *rec = a.spart + (size_t)ul * ns * g * rs;
+  int li, bi, h;
+  unit_coords(a, ul, li, bi, h);
+  if (tid < g) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; s++) {
+      const float *r = rec + ((size_t)s * g + tid) * rs;
+      if (r[1] > 0.f) M = fmaxf(M, r[0]);
+    }
+    float L = 0.f;
+    for (int s = 0; s < ns; s++) {
+      const float *r = rec + ((size_t)s * g + tid) * rs;
+      if (r[1] > 0.f) L += r[1] * __expf(r[0] - M);
+    }
+    fac[tid][0] = M;
+    fac[tid][1] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < g * (rsV + D); idx += NT) {
+    const int hh = idx / (rsV + D), t = idx - hh * (rsV + D);
+    float v = 0.f;
+    for (int s = 0; s < ns; s++) {
+      const float *r = rec + ((size_t)s * g + hh) * rs;
+      if (r[1] > 0.f) v += __expf(r[0] - fac[hh][0]) * r[2 + t];
+    }
+    if (t < rsV)
+      op[hh][t] = v;
+    else
+      ow[hh][t - rsV] = v;
+  }
+  __syncthreads();
+  const float *Bv = a.L.X[1].Bt + (size_t)u * rsV * D;
+  float *out = (float *)a.out + (((size_t)bi * a.nl_in + a.lrel0 + li) * a.L.qh + (size_t)h * g) * D;
+  for (int idx = tid; idx < g * D; idx += NT) {
+    const int hh = idx / D, t = idx - hh * D;
+    float s = ow[hh][t];
+    for (int j = 0; j < a.kV; j++) s += op[hh][j] * Bv[(size_t)j * D + t];
+    out[idx] = s / fac[hh][1];
+  }
+}
+
 template <int KS, int NTV>
 hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
   DecodeArgs a = a0;
@@ -871,10 +952,20 @@ hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
   size_t lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, ew);
   a.wlds = (ew > 0 && lds <= 160 * 1024 && ((uintptr_t)a.q & 15) == 0) ? 1 : 0;
   if (!a.wlds) lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, 0);
-  hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV>,
+  if (a.nsplit > 0) {
+    hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_decode_unit<KS, NTV, true>), dim3(nunits, a.nsplit), dim3(NTU), lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_decode_merge, dim3(nunits), dim3(NT), 0, s, a);
+    return hipGetLastError();
+  }
+  hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_unit<KS, NTV>), dim3(nunits), dim3(NTU), lds, s, a);
+  hipLaunchKernelGGL((k_decode_unit<KS, NTV, false>), dim3(nunits), dim3(NTU), lds, s, a);
   return hipGetLastError();
 }
 
@@ -910,6 +1001,11 @@ bool decode_can_fuse(const DecodeArgs &a) {
   if (!(a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0)) return false;
   if ((((uintptr_t)a.q | (uintptr_t)a.nk | (uintptr_t)a.nv) & 15) != 0) return false;
   return decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, a.e + 1) <= 160 * 1024;
+}
+
+bool decode_can_split(const DecodeArgs &a) {
+  if (!(a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0)) return false;
+  return a.nnew == 0;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
