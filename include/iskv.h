@@ -58,8 +58,12 @@ typedef enum {
   ISKV_ERR_HIP = -4,       /* a HIP runtime call failed */
   ISKV_ERR_NUMERIC = -5,   /* returned by iskv_status when a numeric flag is set */
   ISKV_ERR_POISONED = -6,  /* an earlier launch failed; the handle is unusable */
-  ISKV_ERR_STATE = -7      /* call not valid in the current state (e.g. empty cache) */
+  ISKV_ERR_STATE = -7,     /* call not valid in the current state (e.g. empty cache) */
+  ISKV_ERR_SCRATCH = -8    /* the call would need more than the static scratch array */
 } iskv_status_code;
+
+/* Bytes of the library's static device array used by iskv_decode_attn_static. */
+#define ISKV_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1 } iskv_dtype;
 
@@ -159,6 +163,25 @@ ISKV_API int iskv_prefill_block(iskv_t h, const void *k_rows, const void *v_rows
  * layer in range must hold at least one token (else ISKV_ERR_STATE). */
 ISKV_API int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers,
                      float scale, void *stream);
+
+/* Allocation-free iskv_decode_attn, for callers that cannot allocate device
+ * memory or call an allocating routine (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid it). Same arguments, layouts and
+ * results as iskv_decode_attn (to rounding: the history of each unit is split
+ * over several workgroups whose partial softmax sums are merged by
+ * log-sum-exp). The partials live in a static device array of
+ * ISKV_STATIC_SCRATCH_BYTES owned by the library, one per GPU, held until the
+ * process ends; nothing in it needs clearing (each call writes every partial
+ * it reads). Calls that overlap on one GPU (any handle, any stream) race on
+ * that array: serialize them. Requires bf16 coordinates and rows and ranks
+ * that are multiples of 8 (else ISKV_ERR_ARG); a call whose partials exceed
+ * the array (units x splits x g x (2 + r_V + d) floats, at least one split per
+ * unit) returns ISKV_ERR_SCRATCH; ISKV_ERR_HIP if the array's device address
+ * could not be obtained at iskv_init. All checks happen before anything is
+ * enqueued. This function calls no hipMalloc, hipFree or other allocating
+ * routine. */
+ISKV_API int iskv_decode_attn_static(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers,
+                                     float scale, void *stream);
 
 /* One decode step in one call: append one new K and V row per sequence and
  * kv head (as iskv_append_block with nrows = 1), then decode attention over

@@ -6,12 +6,42 @@
 // holds w + b rows).
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "iskv.h"
 #include "iskv_internal.hpp"
 
 using namespace iskv;
+
+// Device memory owned by the library for iskv_decode_attn_static: the split
+// decode partials of callers that cannot allocate. Each GPU the library runs
+// on holds its own copy until the process ends. Host code never uses the
+// symbol itself (on the host it is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device, at the
+// first iskv_init on that device.
+static __device__ __align__(256) unsigned char scratch[ISKV_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+bool g_scratch_done[MAX_DEVICES];
+
+// device address of `scratch` on the current device (nullptr if unavailable)
+void *static_scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_done[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = (e == hipSuccess) ? ptr : nullptr;
+    g_scratch_done[dev] = true;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
 
 struct iskv_ctx {
   iskv_config cfg;
@@ -24,6 +54,7 @@ struct iskv_ctx {
   // caller's timing events recorded around each fold's kernels (see iskv_set_fold_events)
   hipEvent_t fev[4];
   bool fev_on;
+  void *static_scratch;  // device address of `scratch` on the handle's device (or nullptr)
 };
 
 static_assert(MODE_JOINT == ISKV_MODE_JOINT && MODE_FIXED_COORDS == ISKV_MODE_FIXED_COORDS &&
@@ -268,6 +299,7 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *strea
   h->poisoned = false;
   h->mode = ISKV_MODE_JOINT;
   h->fev_on = false;
+  h->static_scratch = static_scratch_for_current_device();
   if (launch_zero(dev_ws, need, (hipStream_t)stream) != hipSuccess) {
     delete h;
     return ISKV_ERR_HIP;
@@ -459,6 +491,39 @@ int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer0, int32_
   return ISKV_OK;
 }
 
+int iskv_decode_attn_static(iskv_t h, const void *q, float *out, int32_t layer0, int32_t nlayers, float scale,
+                            void *stream) {
+  if (!h || !q || !out) return ISKV_ERR_ARG;
+  if (h->poisoned) return ISKV_ERR_POISONED;
+  if (bad_layers(h, layer0, nlayers)) return ISKV_ERR_ARG;
+  for (int l = layer0; l < layer0 + nlayers; l++)
+    if (h->n[l] + h->e[l] == 0) return ISKV_ERR_STATE;
+  if (!h->static_scratch) return ISKV_ERR_HIP;
+  // every launch is planned (and checked against the array) before any is enqueued
+  std::vector<DecodeArgs> plan;
+  for (int l0 = layer0; l0 < layer0 + nlayers;) {
+    const int l1 = run_end(h, l0, layer0 + nlayers);
+    DecodeArgs a = decode_args(h, q, out, layer0, nlayers, l0, l1, scale);
+    if (!decode_can_split(a)) return ISKV_ERR_ARG;
+    const int nunits = h->L.batch * (l1 - l0) * h->L.kvh;
+    const size_t per = decode_split_floats(h->L.g, h->L.X[1].r) * sizeof(float);
+    choose_split(a, nunits, 64, (float *)h->static_scratch, true);
+    if ((size_t)nunits * a.nsplit * per > ISKV_STATIC_SCRATCH_BYTES) {
+      a.nsplit = 0;
+      choose_split(a, 1 << 20, 1, (float *)h->static_scratch, true);  // one partial per unit
+      if ((size_t)nunits * a.nsplit * per > ISKV_STATIC_SCRATCH_BYTES) return ISKV_ERR_SCRATCH;
+    }
+    plan.push_back(a);
+    l0 = l1;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (const DecodeArgs &a : plan) {
+    const int rc = fail_hip(h, launch_decode(a, s));
+    if (rc) return rc;
+  }
+  return ISKV_OK;
+}
+
 int iskv_append_decode(iskv_t h, const void *k_rows, const void *v_rows, const void *q, float *out,
                        int32_t layer0, int32_t nlayers, float scale, void *stream) {
   if (!h || !k_rows || !v_rows || !q || !out) return ISKV_ERR_ARG;
@@ -630,6 +695,7 @@ const char *iskv_strerror(int code) {
     case ISKV_ERR_NUMERIC: return "numeric flag set (sweep cap or non-finite value)";
     case ISKV_ERR_POISONED: return "handle poisoned by an earlier launch failure";
     case ISKV_ERR_STATE: return "call not valid in the current cache state";
+    case ISKV_ERR_SCRATCH: return "call needs more than the library's static scratch array";
     default: return "unknown status";
   }
 }

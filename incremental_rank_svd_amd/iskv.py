@@ -24,6 +24,7 @@ ISKV_ERR_HIP = -4
 ISKV_ERR_NUMERIC = -5
 ISKV_ERR_POISONED = -6
 ISKV_ERR_STATE = -7
+ISKV_ERR_SCRATCH = -8
 
 ISKV_F32 = 0
 ISKV_BF16 = 1
@@ -36,7 +37,7 @@ EXPORTED = [
     "iskv_prefill_oneshot",
     "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
-    "iskv_set_fold_events",
+    "iskv_set_fold_events", "iskv_decode_attn_static",
 ]
 
 
@@ -75,6 +76,7 @@ def load(path: str = None):
     lib.iskv_append_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
     lib.iskv_prefill_block.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
     lib.iskv_decode_attn.argtypes = [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
+    lib.iskv_decode_attn_static.argtypes = [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
     lib.iskv_append_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]
     lib.iskv_reconstruct.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
     P32 = ctypes.POINTER(_i32)
@@ -215,6 +217,21 @@ class Cache:
         s = float(c.head_dim ** -0.5) if scale is None else float(scale)
         _check(self.lib.iskv_decode_attn(self.h, qp, op, layer0, nl, ctypes.c_float(s), _stream(stream)),
                "iskv_decode_attn")
+        return out
+
+    def decode_attn_static(self, q, out=None, layer0=0, scale=None, stream=None):
+        """iskv_decode_attn_static: decode attention with its partials in the
+        library's static device array (no allocation by the library)."""
+        c = self.cfg
+        nl = q.shape[1]
+        shape = (c.batch, nl, c.q_heads, c.head_dim)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        qp = self._t(q, shape, self.kv_dtype, "q")
+        op = self._t(out, shape, torch.float32, "out")
+        s = float(c.head_dim ** -0.5) if scale is None else float(scale)
+        _check(self.lib.iskv_decode_attn_static(self.h, qp, op, layer0, nl, ctypes.c_float(s), _stream(stream)),
+               "iskv_decode_attn_static")
         return out
 
     def append_decode(self, k_rows, v_rows, q, out=None, layer0=0, scale=None, stream=None):
