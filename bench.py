@@ -374,7 +374,7 @@ def fold_decode_bench(args, w):
     rw_b /= args.steps
     dec_b /= args.steps
     kern = {
-        "k_core": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": 157.3,
+        "k_fold": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": 157.3,
                    "unit": "TFLOP/s", "avg_launch_ms": avg["core"], "work_per_launch": core_f,
                    "sweeps": [sw[0], sw[1]]},
         "k_rewrite_mfma": {"bound": "hbm", "achieved": rw_b / (avg["rewrite"] * 1e-3) / 1e9,
