@@ -610,8 +610,11 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   __syncthreads();
   float *Eg = Pg;                          // kplus x kplus: E
   float *Gg = Pg + (size_t)kplus * kplus;  // kplus x kplus: E/2 - E_H
-  for (int e = tid; e < kplus * kplus; e += NTF) {
-    const int i = e / kplus, j = e - i * kplus;
+  // both Gram matrices are symmetric (each entry's sums run in an order
+  // symmetric in i and j), so one triangle is computed and mirrored
+  for (int e = tid; e < kplus * (kplus + 1) / 2; e += NTF) {
+    int i, j;
+    tri_index(e, j, i);  // i <= j
     const float *bi = Bp + (size_t)i * D, *bj = Bp + (size_t)j * D;
     double acc = 0.0;
 #pragma unroll 2
@@ -626,8 +629,11 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     for (int l = 0; l < c; l++) ah += (double)hi[l] * hj[l];
     ah *= (double)(sgn[i] * sgn[j]);
     const double dl = (i == j) ? 1.0 : 0.0;
-    Eg[e] = (float)(acc - dl);
-    Gg[e] = (float)(0.5 * (acc - dl) - (ah - dl));
+    const float ev = (float)(acc - dl), gv = (float)(0.5 * (acc - dl) - (ah - dl));
+    Eg[(size_t)i * kplus + j] = ev;
+    Eg[(size_t)j * kplus + i] = ev;
+    Gg[(size_t)i * kplus + j] = gv;
+    Gg[(size_t)j * kplus + i] = gv;
   }
   __syncthreads();
   {

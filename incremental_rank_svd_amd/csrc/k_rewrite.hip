@@ -102,6 +102,13 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// two fp32 values to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 constexpr int RG = 4;  // 16-row groups in flight per wavefront (each H fragment serves all of them)
 constexpr int HP = 3;  // bf16 parts of H_top
 
@@ -145,9 +152,9 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
   uint16_t *C = (uint16_t *)X.C + (size_t)u * X.cstride;
   const int ngroups = (a.n + 15) / 16;
   const int gstride = gridDim.x * (NT / 64);
-  for (int g0 = blockIdx.x * (NT / 64) + wv; g0 < ngroups; g0 += RG * gstride) {
-    // every row of these groups is read before any of them is written
-    u32x4_t cf[RG][4];
+  // the RG groups of the next iteration are loaded while the current ones are
+  // computed (their rows are disjoint from the rows being written)
+  auto load_groups = [&](int g0, u32x4_t (&cf)[RG][4]) {
 #pragma unroll
     for (int q = 0; q < RG; q++) {
       const int row = (g0 + q * gstride) * 16 + (lane & 15);
@@ -159,31 +166,51 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
           cf[q][s] = *reinterpret_cast<const u32x4_t *>(C + (size_t)row * r + kb);
       }
     }
-    // each H fragment is read from LDS once for all RG groups
-    for (int t = 0; t < T; t++) {
-      f32x4_t acc[RG];
+  };
+  u32x4_t cf[RG][4], cn[RG][4];
+  const int gfirst = blockIdx.x * (NT / 64) + wv;
+  if (gfirst < ngroups) load_groups(gfirst, cn);
+  for (int g0 = gfirst; g0 < ngroups; g0 += RG * gstride) {
 #pragma unroll
-      for (int q = 0; q < RG; q++) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < RG; q++)
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        if (s < S) {
-          const u32x4_t *fp = fr + (size_t)((t * S + s) * HP) * 64 + lane;
+      for (int s = 0; s < 4; s++) cf[q][s] = cn[q][s];
+    if (g0 + RG * gstride < ngroups) load_groups(g0 + RG * gstride, cn);
+    // each H fragment is read from LDS once for all RG groups; the output
+    // tiles stay in registers so that each row's T chunks are stored back to
+    // back (stored as they come, a row's 32-byte pieces reach memory at
+    // different times and cost whole-line writes each)
+    uint2 ob[RG][8];
 #pragma unroll
-          for (int part = 0; part < HP; part++) {
-            const u32x4_t f = fp[64 * part];
+    for (int t = 0; t < 8; t++) {
+      if (t < T) {
+        f32x4_t acc[RG];
 #pragma unroll
-            for (int q = 0; q < RG; q++) acc[q] = mfma_bf16(f, cf[q][s], acc[q]);
+        for (int q = 0; q < RG; q++) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          if (s < S) {
+            const u32x4_t *fp = fr + (size_t)((t * S + s) * HP) * 64 + lane;
+#pragma unroll
+            for (int part = 0; part < HP; part++) {
+              const u32x4_t f = fp[64 * part];
+#pragma unroll
+              for (int q = 0; q < RG; q++) acc[q] = mfma_bf16(f, cf[q][s], acc[q]);
+            }
           }
         }
-      }
-      const int j0 = 16 * t + 4 * (lane >> 4);
 #pragma unroll
-      for (int q = 0; q < RG; q++) {
-        const int row = (g0 + q * gstride) * 16 + (lane & 15);
-        if (row < a.n && j0 < r) {
-          const uint32_t lo = (uint32_t)f2bf(acc[q][0]) | ((uint32_t)f2bf(acc[q][1]) << 16);
-          const uint32_t hi = (uint32_t)f2bf(acc[q][2]) | ((uint32_t)f2bf(acc[q][3]) << 16);
-          *reinterpret_cast<uint2 *>(C + (size_t)row * r + j0) = uint2{lo, hi};
+        for (int q = 0; q < RG; q++) ob[q][t] = uint2{pack_bf16(acc[q][0], acc[q][1]), pack_bf16(acc[q][2], acc[q][3])};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RG; q++) {
+      const int row = (g0 + q * gstride) * 16 + (lane & 15);
+      if (row < a.n) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          const int j0 = 16 * t + 4 * (lane >> 4);
+          if (t < T && j0 < r) *reinterpret_cast<uint2 *>(C + (size_t)row * r + j0) = ob[q][t];
         }
       }
     }
