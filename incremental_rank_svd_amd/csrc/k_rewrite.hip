@@ -96,6 +96,7 @@ __global__ void __launch_bounds__(NT) k_rewrite_vec(const RewriteArgs a) {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -109,16 +110,25 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-constexpr int RG = 4;  // 16-row groups in flight per wavefront (each H fragment serves all of them)
+// 16-row groups in flight per wavefront (each H fragment serves all of them):
+// four, three for the largest ranks, whose registers would not fit two waves
+// per SIMD otherwise
+template <int T>
+constexpr int row_groups() { return T >= 7 ? 3 : 4; }
 constexpr int HP = 3;  // bf16 parts of H_top
 
-template <int XK>
-__device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t *fr) {
+// T = ceil(r / 16) output column tiles (columns kp .. r-1 come out zero) is a
+// template constant, so that a rank's register arrays hold only its own
+// tiles and K steps (at most ceil(T / 2)).
+template <int T, int XK>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_rewrite_mfma(const RewriteArgs a) {
+  extern __shared__ u32x4_t fr[];
+  constexpr int SM = (T + 1) / 2;
+  constexpr int RG = row_groups<T>();
   const Stream &X = a.X[XK];
   const int k = a.k[XK], kp = a.kp[XK], r = a.r[XK];
   if (a.n <= 0 || k <= 0) return;
-  const int S = (k + 31) / 32;  // K steps
-  const int T = (r + 15) / 16;  // output column tiles (columns kp .. r-1 come out zero)
+  const int S = (k + 31) / 32;  // K steps, at most SM
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int u = a.u0 + blockIdx.y;
   const float *Ht = X.Htop + (size_t)u * r * r;
@@ -152,43 +162,65 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
   uint16_t *C = (uint16_t *)X.C + (size_t)u * X.cstride;
   const int ngroups = (a.n + 15) / 16;
   const int gstride = gridDim.x * (NT / 64);
-  // the RG groups of the next iteration are loaded while the current ones are
-  // computed (their rows are disjoint from the rows being written)
-  auto load_groups = [&](int g0, u32x4_t (&cf)[RG][4]) {
+  // The unit's rows are read and written through a buffer resource whose
+  // range is the n stored rows: an access past it reads zeros and writes
+  // nothing, so rows past n and 16-byte chunks past column r (their offset is
+  // pushed above 2^31, out of the range) need no branch and no select.
+  // The RG groups of the next iteration are loaded while the current ones are
+  // computed (their rows are disjoint from the rows being written).
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(C, (short)0, a.n * r * 2, 0x00020000);
+  // (offsets are unsigned 32-bit; the launcher keeps every row offset below 2^31)
+  constexpr uint32_t OUT = 0x80000000u;
+  const int kq = 8 * (lane >> 4), jq = 4 * (lane >> 4);
+  auto coff = [&](int s) { return 32 * s + kq < r ? 2u * (32 * s + kq) : OUT; };
+  // Output staging: one 16-row group per wave in LDS after the fragments,
+  // rows RS bytes apart (room for T whole tiles plus 16 bytes against bank
+  // conflicts). A lane writes its 8-byte pieces of a row there, then the
+  // group (16 rows of 2r bytes, contiguous in memory) is read back and
+  // stored as 16 contiguous bytes per lane: whole lines per instruction.
+  constexpr int RS = 32 * T + 16, NI = (T + 1) / 2;  // 16 * 32T bytes <= NI KiB
+  char *stg = reinterpret_cast<char *>(fr + (size_t)T * S * HP * 64) + wv * 16 * RS;
+  char *stw = stg + (lane & 15) * RS + 2 * jq;
+  uint32_t sl[NI], so[NI];
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    const int off = 1024 * i + 16 * lane, row = off / (2 * r), col = off - row * 2 * r;
+    const bool in = off < 32 * r;
+    sl[i] = in ? row * RS + col : 0;
+    so[i] = in ? (uint32_t)off : OUT;
+  }
+  auto load_groups = [&](int g0, u32x4_t (&cf)[RG][SM]) {
 #pragma unroll
     for (int q = 0; q < RG; q++) {
-      const int row = (g0 + q * gstride) * 16 + (lane & 15);
+      const uint32_t ro = (uint32_t)((g0 + q * gstride) * 16 + (lane & 15)) * (uint32_t)(2 * r);
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        const int kb = 32 * s + 8 * (lane >> 4);
-        cf[q][s] = u32x4_t{0u, 0u, 0u, 0u};
-        if (s < S && row < a.n && kb < r)
-          cf[q][s] = *reinterpret_cast<const u32x4_t *>(C + (size_t)row * r + kb);
-      }
+      for (int s = 0; s < SM; s++)
+        cf[q][s] = s < S ? __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(ro + coff(s)), 0, 0)
+                         : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  u32x4_t cf[RG][4], cn[RG][4];
+  u32x4_t cf[RG][SM], cn[RG][SM];
   const int gfirst = blockIdx.x * (NT / 64) + wv;
   if (gfirst < ngroups) load_groups(gfirst, cn);
   for (int g0 = gfirst; g0 < ngroups; g0 += RG * gstride) {
 #pragma unroll
     for (int q = 0; q < RG; q++)
 #pragma unroll
-      for (int s = 0; s < 4; s++) cf[q][s] = cn[q][s];
+      for (int s = 0; s < SM; s++) cf[q][s] = cn[q][s];
     if (g0 + RG * gstride < ngroups) load_groups(g0 + RG * gstride, cn);
     // each H fragment is read from LDS once for all RG groups; the output
-    // tiles stay in registers so that each row's T chunks are stored back to
-    // back (stored as they come, a row's 32-byte pieces reach memory at
-    // different times and cost whole-line writes each)
-    uint2 ob[RG][8];
+    // tiles stay in registers until all T are done, then each group goes to
+    // memory through the wave's LDS staging rows as whole contiguous rows
+    u32x2_t ob[RG][T];
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-      if (t < T) {
+    for (int t = 0; t < T; t++) {
+      {
         f32x4_t acc[RG];
 #pragma unroll
         for (int q = 0; q < RG; q++) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
+        for (int s = 0; s < SM; s++) {
           if (s < S) {
             const u32x4_t *fp = fr + (size_t)((t * S + s) * HP) * 64 + lane;
 #pragma unroll
@@ -200,50 +232,73 @@ __device__ __forceinline__ void rewrite_mfma_body(const RewriteArgs &a, u32x4_t 
           }
         }
 #pragma unroll
-        for (int q = 0; q < RG; q++) ob[q][t] = uint2{pack_bf16(acc[q][0], acc[q][1]), pack_bf16(acc[q][2], acc[q][3])};
+        for (int q = 0; q < RG; q++) ob[q][t] = u32x2_t{pack_bf16(acc[q][0], acc[q][1]), pack_bf16(acc[q][2], acc[q][3])};
+        // keep the scheduler from overlapping tiles (each tile's accumulators
+        // would stay live, and the registers of large ranks run out)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int q = 0; q < RG; q++) {
-      const int row = (g0 + q * gstride) * 16 + (lane & 15);
-      if (row < a.n) {
 #pragma unroll
-        for (int t = 0; t < 8; t++) {
-          const int j0 = 16 * t + 4 * (lane >> 4);
-          if (t < T && j0 < r) *reinterpret_cast<uint2 *>(C + (size_t)row * r + j0) = ob[q][t];
-        }
-      }
+      for (int t = 0; t < T; t++) *reinterpret_cast<u32x2_t *>(stw + 32 * t) = ob[q][t];
+      // other lanes of this wave read what it wrote (a wave's LDS accesses
+      // complete in order; the fences keep the compiler from moving them)
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint32_t go = (uint32_t)(g0 + q * gstride) * (uint32_t)(32 * r);
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t *>(stg + sl[i]), rs,
+                                               (int)(go + so[i]), 0, 0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
   }
 }
 
-__global__ void __launch_bounds__(NT) k_rewrite_mfma(const RewriteArgs a) {
-  extern __shared__ u32x4_t fr[];
-  if (blockIdx.z == 0)
-    rewrite_mfma_body<0>(a, fr);
+template <int T>
+hipError_t launch_rewrite_t(const RewriteArgs &a, int x, dim3 grid, size_t lds, hipStream_t s) {
+  const void *f = x == 0 ? (const void *)k_rewrite_mfma<T, 0> : (const void *)k_rewrite_mfma<T, 1>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (x == 0)
+    hipLaunchKernelGGL((k_rewrite_mfma<T, 0>), grid, dim3(NT), lds, s, a);
   else
-    rewrite_mfma_body<1>(a, fr);
+    hipLaunchKernelGGL((k_rewrite_mfma<T, 1>), grid, dim3(NT), lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s) {
   if (a.n <= 0 || nunits <= 0) return hipSuccess;
-  if (coord_bf16 && a.r[0] % 8 == 0 && a.r[1] % 8 == 0) {
-    size_t lds = 0;
-    for (int x = 0; x < 2; x++) {
-      const size_t l = (size_t)((a.r[x] + 15) / 16) * ((a.k[x] + 31) / 32) * HP * 64 * 16;
-      if (l > lds) lds = l;
-    }
+  // matrix-core path: bf16 rows 16-byte aligned, and every row offset the
+  // kernel forms (up to n plus the rows of one prefetch, in bytes) below 2^31
+  const int rmax = a.r[0] > a.r[1] ? a.r[0] : a.r[1];
+  if (coord_bf16 && a.r[0] % 8 == 0 && a.r[1] % 8 == 0 &&
+      ((size_t)a.n + 65536) * rmax * 2 < ((size_t)1 << 31)) {
     // about 2048 rows per workgroup (the H fragments are built once per
-    // workgroup), at most 64 workgroups per unit and kind
+    // workgroup), at most 64 workgroups per unit; one launch per kind
     int tiles = (a.n + 2047) / 2048;
     if (tiles > 64) tiles = 64;
-    hipError_t e = hipFuncSetAttribute((const void *)k_rewrite_mfma,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_rewrite_mfma, dim3(tiles, nunits, 2), dim3(NT), lds, s, a);
-    return hipGetLastError();
+    for (int x = 0; x < 2; x++) {
+      if (a.k[x] <= 0) continue;
+      const int T = (a.r[x] + 15) / 16;
+      const size_t lds = (size_t)T * ((a.k[x] + 31) / 32) * HP * 64 * 16 + (size_t)(NT / 64) * 16 * (32 * T + 16);
+      const dim3 grid(tiles, nunits, 1);
+      hipError_t e;
+      switch ((a.r[x] + 15) / 16) {
+        case 1: e = launch_rewrite_t<1>(a, x, grid, lds, s); break;
+        case 2: e = launch_rewrite_t<2>(a, x, grid, lds, s); break;
+        case 3: e = launch_rewrite_t<3>(a, x, grid, lds, s); break;
+        case 4: e = launch_rewrite_t<4>(a, x, grid, lds, s); break;
+        case 5: e = launch_rewrite_t<5>(a, x, grid, lds, s); break;
+        case 6: e = launch_rewrite_t<6>(a, x, grid, lds, s); break;
+        case 7: e = launch_rewrite_t<7>(a, x, grid, lds, s); break;
+        default: e = launch_rewrite_t<8>(a, x, grid, lds, s); break;
+      }
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   size_t lds = 0;
   for (int x = 0; x < 2; x++) {

@@ -143,15 +143,21 @@ def test_gqa_multi_unit(iskv, coord):
 def _rotation_check(C0, B0, k0, n, C1, B1, k1):
     """Old rows after a fold against C_old (B_old B_new^T) in fp64, which is
     C_old H_top for any correct fold (B_new = [B_old P] H, B_old P = 0):
-    every value within one bf16 ulp of the rounded product for all but
-    1e-3 of them; returns the max deviation relative to the largest value."""
+    every value within one bf16 ulp of the rounded product, plus the fp32
+    floor of a k-term product (16 fp32 ulps of the row's norm: H_top and
+    the basis are fp32 and re-orthonormalised to first order, so values far
+    below their row's norm carry that absolute error), for all but 1e-3 of
+    them; returns the max deviation relative to the largest value."""
     Ht = B0[:k0] @ B1[:k1].T  # k0 x k1
     ref = C0[:n, :k0] @ Ht
     ref_bf = synth.bf16_round(ref).astype(np.float64)
     got = C1[:n, :k1]
     _, ex = np.frexp(ref_bf)
     ulp = np.ldexp(1.0, ex - 8)  # one bf16 ulp at each value
-    over = np.abs(got - ref_bf) > ulp * 1.0001
+    floor32 = 16 * 2.0 ** -24 * np.linalg.norm(C0[:n, :k0], axis=1, keepdims=True)
+    over = np.abs(got - ref_bf) > ulp * 1.0001 + floor32
+    note("  beyond 1 ulp: %.2e, beyond 1 ulp + fp32 floor: %.2e"
+         % ((np.abs(got - ref_bf) > ulp * 1.0001).mean(), over.mean()))
     assert over.mean() <= 1e-3, over.mean()
     assert np.all(C1[:n, k1:] == 0)
     return float(np.abs(got - ref).max() / np.abs(ref).max())
@@ -162,6 +168,8 @@ def _rotation_check(C0, B0, k0, n, C1, B1, k1):
     dict(rank_k=24, rank_v=48, block=64, window=128),    # ragged K step, T = 2 and 3
     dict(rank_k=96, rank_v=64, block=64, window=64),     # the rank grows 64 -> 96 at the second fold
     dict(rank_k=64, rank_v=96, block=128, window=256),   # the 13B-MHA shape: S = 2 and 3, T = 4 and 6
+    dict(rank_k=128, rank_v=16, block=64, window=64),    # T = 8 (S up to 4, three row groups) and T = 1
+    dict(rank_k=80, rank_v=112, block=64, window=64),    # T = 5 and 7, ragged last K step
 ])
 def test_rewrite_is_rotation_of_stored_rows(iskv, shape):
     """Each of the second to fourth folds rewrites every old row as
