@@ -187,6 +187,65 @@ __device__ __forceinline__ void house_qr(float *A, int ld, int nrows, int ncols,
   }
 }
 
+// Matrix-core products. v_mfma_f32_16x16x4_f32 and v_mfma_f64_16x16x4_f64
+// take, from lane l of the wavefront, A[l % 16][l / 16] and B[l / 16][l % 16]
+// of one 16 x 16 x 4 step. Element v of lane l's accumulator then holds
+// D[4 (l / 16) + v][l % 16] (fp32) or D[l / 16 + 4 v][l % 16] (fp64).
+typedef __attribute__((ext_vector_type(4))) float mf32x4;
+typedef __attribute__((ext_vector_type(4))) double mf64x4;
+
+__device__ __forceinline__ mf32x4 mfma4_f32(float a, float b, mf32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ mf64x4 mfma4_f64(double a, double b, mf64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// sum_k a(i, k) b(k, j) over the 16 x 16 tiles covering M x N, in fp32 on
+// matrix cores; the NW waves of the workgroup take the tiles in turn. fa / fb
+// are called for i < 16 ceil(M/16), k < 16 ceil(K/16), j < 16 ceil(N/16) and
+// return 0 outside the matrices. epi(i0, j0, acc) is called by the whole
+// wave for each tile (lane l holds rows i0 + 4 (l/16) + v, column j0 + l%16).
+// Two accumulation chains (even and odd K steps) keep consecutive
+// matrix-core operations independent.
+template <int NW, typename FA, typename FB, typename FE>
+__device__ __forceinline__ void mfma_gemm_tiles_f32(int M, int N, int K, FA fa, FB fb, FE epi) {
+  const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63, l16 = ln & 15, lk = ln >> 4;
+  const int tn = (N + 15) >> 4, nt = ((M + 15) >> 4) * tn;
+  for (int t = wv; t < nt; t += NW) {
+    const int ti = t / tn;
+    const int i0 = 16 * ti, j0 = 16 * (t - ti * tn);
+    mf32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    // four K steps per iteration, their operands loaded before the first
+    // product (steps past K multiply zeros; matrix-core loops are not
+    // unrolled by the compiler)
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int z = 0; z < 4; z++) {
+        av[z] = fa(i0 + l16, k0 + 4 * z + lk);
+        bv[z] = fb(k0 + 4 * z + lk, j0 + l16);
+      }
+      c0 = mfma4_f32(av[0], bv[0], c0);
+      c1 = mfma4_f32(av[1], bv[1], c1);
+      c0 = mfma4_f32(av[2], bv[2], c0);
+      c1 = mfma4_f32(av[3], bv[3], c1);
+    }
+    epi(i0, j0, c0 + c1);
+  }
+}
+
+// the same, with out(i, j, value) called for every position of every tile
+// (it checks i < M, j < N itself)
+template <int NW, typename FA, typename FB, typename FO>
+__device__ __forceinline__ void mfma_gemm_f32(int M, int N, int K, FA fa, FB fb, FO out) {
+  const int ln = threadIdx.x & 63, l16 = ln & 15, lk = ln >> 4;
+  mfma_gemm_tiles_f32<NW>(M, N, K, fa, fb, [&](int i0, int j0, mf32x4 acc) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) out(i0 + 4 * lk + v, j0 + l16, acc[v]);
+  });
+}
+
 // Cyclic sweeps of one-sided Jacobi over the c columns of J (column stride
 // sj; LP lanes per column pair, lane o holding the contiguous rows
 // o * 4NQ .. o * 4NQ + 4NQ - 1; rows past the column length are zero) without

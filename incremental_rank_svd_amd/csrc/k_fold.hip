@@ -57,7 +57,7 @@ __host__ __device__ inline FoldLds fold_lds(int k, int b, int r) {
   const int sj = fold_sj(c);
   const int a = m * LDA;                   // [B | E^T] as rows
   const int h = c * sj;                    // R^T / H
-  const int bp = kp * (D > sj ? D : sj);  // B+ staging, then H_r G
+  const int bp = kp * (LDA > sj ? LDA : sj);  // B+ staging (stride LDA), then H_r G (stride sj)
   int big = a;
   if (h + bp > big) big = h + bp;
   L.big = (big + 3) / 4 * 4;
@@ -527,54 +527,19 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   }
   __syncthreads();
 
-  // B+ = [B P] H_r into the second region (rows j' x D), 64 rows at a time
+  // The products below run on matrix cores (fp32, the Gram matrices fp64).
+  constexpr int NW = NTF / 64;
+  // B+ = [B P] H_r into the second region (rows j' x D, stride LDA)
   float *Bp = smem + (size_t)c * sj;
-  {
-    const int cq = tid & 31;  // columns 4cq .. 4cq+3
-    const int rg = tid >> 5;  // rows rg, rg+16, rg+32, rg+48 of each chunk
-    for (int j0 = 0; j0 < kplus; j0 += 64) {
-      float acc[4][4];
-#pragma unroll
-      for (int z = 0; z < 4; z++)
-#pragma unroll
-        for (int t = 0; t < 4; t++) acc[z][t] = 0.f;
-      for (int i0 = 0; i0 < c; i0 += 8) {
-        float4 bp[8];  // eight rows of [B; P] in flight at once
-#pragma unroll
-        for (int ii = 0; ii < 8; ii++) {
-          const int i = i0 + ii;
-          bp[ii] = float4{0.f, 0.f, 0.f, 0.f};
-          if (i < c) {
-            const float *src = (i < k) ? (Bt + (size_t)i * D) : (Pg + (size_t)(i - k) * D);
-            bp[ii] = *reinterpret_cast<const float4 *>(src + 4 * cq);
-          }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 8; ii++) {
-          const int i = i0 + ii;
-          if (i < c) {
-#pragma unroll
-            for (int z = 0; z < 4; z++) {
-              const int jr = j0 + rg + 16 * z;
-              if (jr < kplus) {
-                const float hv = H[(size_t)perm[jr] * sj + i];
-                acc[z][0] += hv * bp[ii].x;
-                acc[z][1] += hv * bp[ii].y;
-                acc[z][2] += hv * bp[ii].z;
-                acc[z][3] += hv * bp[ii].w;
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int z = 0; z < 4; z++) {
-        const int jr = j0 + rg + 16 * z;
-        if (jr < kplus)
-          *reinterpret_cast<float4 *>(Bp + (size_t)jr * D + 4 * cq) = float4{acc[z][0], acc[z][1], acc[z][2], acc[z][3]};
-      }
-    }
-  }
+  mfma_gemm_f32<NW>(
+      kplus, D, c,
+      [&](int jr, int i) { return (jr < kplus && i < c) ? H[(size_t)perm[jr] * sj + i] : 0.f; },
+      [&](int i, int d) {
+        return i < c ? ((i < k) ? Bt[(size_t)i * D + d] : Pg[(size_t)(i - k) * D + d]) : 0.f;
+      },
+      [&](int jr, int d, float v) {
+        if (jr < kplus) Bp[(size_t)jr * LDA + d] = v;
+      });
   __syncthreads();
   // sign rule: entry of largest magnitude (lowest index on ties) positive
   for (int jr = grp; jr < kplus; jr += NGR) {
@@ -582,7 +547,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     int bi = 0;
 #pragma unroll
     for (int t = 0; t < 8; t++) {
-      const float v = fabsf(Bp[(size_t)jr * D + lane * 8 + t]);
+      const float v = fabsf(Bp[(size_t)jr * LDA + lane * 8 + t]);
       if (v > best) {
         best = v;
         bi = lane * 8 + t;
@@ -597,7 +562,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
         bi = oi;
       }
     }
-    if (lane == 0) sgn[jr] = (Bp[(size_t)jr * D + bi] < 0.f) ? -1.f : 1.f;
+    if (lane == 0) sgn[jr] = (Bp[(size_t)jr * LDA + bi] < 0.f) ? -1.f : 1.f;
   }
   __syncthreads();
   // Re-orthonormalization (as in the fixed-coordinate core): with
@@ -606,89 +571,83 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   // (a rotation error inflates C+ = Z H_r and B+ alike and is removed from
   // both; a basis error belongs to the coordinates), so C+ B+ is unchanged to
   // O(E^2) and sigma stays the column norms of the stored coordinates.
-  for (int idx = tid; idx < kplus * D; idx += NTF) Bp[idx] *= sgn[idx / D];
+  for (int idx = tid; idx < kplus * D; idx += NTF) Bp[(size_t)(idx / D) * LDA + idx % D] *= sgn[idx / D];
   __syncthreads();
   float *Eg = Pg;                          // kplus x kplus: E
   float *Gg = Pg + (size_t)kplus * kplus;  // kplus x kplus: E/2 - E_H
-  // both Gram matrices are symmetric (each entry's sums run in an order
-  // symmetric in i and j), so one triangle is computed and mirrored
-  for (int e = tid; e < kplus * (kplus + 1) / 2; e += NTF) {
-    int i, j;
-    tri_index(e, j, i);  // i <= j
-    const float *bi = Bp + (size_t)i * D, *bj = Bp + (size_t)j * D;
-    double acc = 0.0;
-#pragma unroll 2
-    for (int t = 0; t < D / 4; t++) {
-      const int v = 4 * ((t + i + j) & (D / 4 - 1));  // rotate the start: fewer bank conflicts
-      const float4 x = *reinterpret_cast<const float4 *>(bi + v);
-      const float4 y = *reinterpret_cast<const float4 *>(bj + v);
-      acc += (double)x.x * y.x + (double)x.y * y.y + (double)x.z * y.z + (double)x.w * y.w;
-    }
-    const float *hi = H + (size_t)perm[i] * sj, *hj = H + (size_t)perm[j] * sj;
-    double ah = 0.0;
-    for (int l = 0; l < c; l++) ah += (double)hi[l] * hj[l];
-    ah *= (double)(sgn[i] * sgn[j]);
-    const double dl = (i == j) ? 1.0 : 0.0;
-    const float ev = (float)(acc - dl), gv = (float)(0.5 * (acc - dl) - (ah - dl));
-    Eg[(size_t)i * kplus + j] = ev;
-    Eg[(size_t)j * kplus + i] = ev;
-    Gg[(size_t)i * kplus + j] = gv;
-    Gg[(size_t)j * kplus + i] = gv;
-  }
-  __syncthreads();
   {
-    // B = (I - E/2) B+ straight to the output basis; lanes own columns, so
-    // every E entry a wave reads is uniform across it
-    const int wv = tid >> 6, ln = tid & 63;
-    constexpr int NW = NTF / 64;
-    float *Btw = X.Bt + (size_t)u * r * D;
-    for (int i0 = 4 * wv; i0 < kplus; i0 += 4 * NW) {
-      float acc[4][2];
-#pragma unroll
-      for (int z = 0; z < 4; z++) acc[z][0] = acc[z][1] = 0.f;
-      for (int l = 0; l < kplus; l++) {
-        const float b0 = Bp[(size_t)l * D + ln], b1 = Bp[(size_t)l * D + ln + 64];
+    // both Gram matrices in fp64 on matrix cores, the tiles of one triangle
+    // only: each entry is computed once and mirrored, so both are exactly
+    // symmetric
+    const int wv = tid >> 6, ln = tid & 63, l16 = ln & 15, lk = ln >> 4;
+    const int tk = (kplus + 15) >> 4;
+    for (int t = wv; t < tk * (tk + 1) / 2; t += NW) {
+      int tj, ti;
+      tri_index(t, tj, ti);  // ti <= tj
+      const int ia = 16 * ti + l16, jb = 16 * tj + l16;
+      const bool va = ia < kplus, vb = jb < kplus;
+      const float *ra = Bp + (size_t)(va ? ia : 0) * LDA, *rb = Bp + (size_t)(vb ? jb : 0) * LDA;
+      mf64x4 e = {0.0, 0.0, 0.0, 0.0}, h = {0.0, 0.0, 0.0, 0.0};
+      for (int d0 = 0; d0 < D; d0 += 16) {
+        double x[4], y[4];
 #pragma unroll
         for (int z = 0; z < 4; z++) {
-          const float ev = (i0 + z < kplus) ? Eg[(size_t)(i0 + z) * kplus + l] : 0.f;
-          acc[z][0] += ev * b0;
-          acc[z][1] += ev * b1;
+          x[z] = va ? (double)ra[d0 + 4 * z + lk] : 0.0;
+          y[z] = vb ? (double)rb[d0 + 4 * z + lk] : 0.0;
         }
+#pragma unroll
+        for (int z = 0; z < 4; z++) e = mfma4_f64(x[z], y[z], e);
+      }
+      const float *ha = H + (size_t)perm[va ? ia : 0] * sj, *hb = H + (size_t)perm[vb ? jb : 0] * sj;
+      for (int l0 = 0; l0 < c; l0 += 16) {
+        double x[4], y[4];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const int l = l0 + 4 * z + lk;
+          x[z] = (va && l < c) ? (double)ha[l] : 0.0;
+          y[z] = (vb && l < c) ? (double)hb[l] : 0.0;
+        }
+#pragma unroll
+        for (int z = 0; z < 4; z++) h = mfma4_f64(x[z], y[z], h);
       }
 #pragma unroll
-      for (int z = 0; z < 4; z++) {
-        const int i = i0 + z;
-        if (i < kplus) {
-          Btw[(size_t)i * D + ln] = Bp[(size_t)i * D + ln] - 0.5f * acc[z][0];
-          Btw[(size_t)i * D + ln + 64] = Bp[(size_t)i * D + ln + 64] - 0.5f * acc[z][1];
+      for (int v = 0; v < 4; v++) {
+        const int i = 16 * ti + lk + 4 * v, j = jb;  // fp64 accumulator layout
+        if (i < kplus && j < kplus && i <= j) {
+          const double dl = (i == j) ? 1.0 : 0.0;
+          const double ah = h[v] * (double)(sgn[i] * sgn[j]);
+          const float ev = (float)(e[v] - dl), gv = (float)(0.5 * (e[v] - dl) - (ah - dl));
+          Eg[(size_t)i * kplus + j] = ev;
+          Eg[(size_t)j * kplus + i] = ev;
+          Gg[(size_t)i * kplus + j] = gv;
+          Gg[(size_t)j * kplus + i] = gv;
         }
       }
     }
+  }
+  __syncthreads();
+  // B = (I - E/2) B+ straight to the output basis
+  {
+    float *Btw = X.Bt + (size_t)u * r * D;
+    mfma_gemm_f32<NW>(
+        kplus, D, kplus,
+        [&](int i, int l) { return (i < kplus && l < kplus) ? Eg[(size_t)i * kplus + l] : 0.f; },
+        [&](int l, int d) { return l < kplus ? Bp[(size_t)l * LDA + d] : 0.f; },
+        [&](int i, int d, float v) {
+          if (i < kplus) Btw[(size_t)i * D + d] = Bp[(size_t)i * LDA + d] - 0.5f * v;
+        });
     for (int idx = kplus * D + tid; idx < r * D; idx += NTF) Btw[idx] = 0.f;
   }
   __syncthreads();  // B+ in the second region is dead from here on
   // Hn = H_r G, signs and rank order applied, column-major (stride sj)
   float *Hn = Bp;
-  {
-    const int wv = tid >> 6, ln = tid & 63;
-    constexpr int NW = NTF / 64;
-    for (int j0 = 4 * wv; j0 < kplus; j0 += 4 * NW) {
-      for (int i = ln; i < c; i += 64) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int l = 0; l < kplus; l++) {
-          const float hv = sgn[l] * H[(size_t)perm[l] * sj + i];
-#pragma unroll
-          for (int z = 0; z < 4; z++)
-            if (j0 + z < kplus) acc[z] += hv * Gg[(size_t)l * kplus + j0 + z];
-        }
-#pragma unroll
-        for (int z = 0; z < 4; z++) {
-          const int jr = j0 + z;
-          if (jr < kplus) Hn[(size_t)jr * sj + i] = sgn[jr] * H[(size_t)perm[jr] * sj + i] + acc[z];
-        }
-      }
-    }
-  }
+  mfma_gemm_f32<NW>(
+      c, kplus, kplus,
+      [&](int i, int l) { return (i < c && l < kplus) ? sgn[l] * H[(size_t)perm[l] * sj + i] : 0.f; },
+      [&](int l, int jr) { return (l < kplus && jr < kplus) ? Gg[(size_t)l * kplus + jr] : 0.f; },
+      [&](int i, int jr, float v) {
+        if (i < c && jr < kplus) Hn[(size_t)jr * sj + i] = sgn[jr] * H[(size_t)perm[jr] * sj + i] + v;
+      });
   __syncthreads();
   {
     float *Ht = X.Htop + (size_t)u * r * r;
@@ -697,33 +656,31 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       Ht[(size_t)i * r + jr] = Hn[(size_t)jr * sj + i];
     }
   }
-  // new rows C[n + i] = [F B | F P]_i Hn (b x k+), staged through the H region
-  float *Ys = H;  // b x c, row stride c (b * c <= c * sj)
-  for (int idx = tid; idx < b * c; idx += NTF) {
-    const int i = idx / c, l = idx - i * c;
-    Ys[idx] = YFP[(size_t)i * D + l];
-  }
-  __syncthreads();
-  // Each thread owns one column and a strided set of rows, so the squared
-  // column norms of the new rows reduce in a fixed order.
-  const int ngrp = NTF / r;
+  // new rows C[n + i] = [F B | F P]_i Hn (b x r, columns k+ .. r-1 zero). The
+  // squared column norms of each 16-row tile go to sqp (the small arrays from
+  // sv on, dead by now: ceil(b/16) r <= 1024 floats) and are summed in a
+  // fixed order below.
+  float *sqp = sv;
   {
     TC *Cn = (TC *)X.C + (size_t)u * X.cstride + (size_t)a.n * r;
-    if (tid < ngrp * r) {
-      const int jr = tid % r, g0 = tid / r;
-      float sq = 0.f;
-      for (int i = g0; i < b; i += ngrp) {
-        float s = 0.f;
-        if (jr < kplus) {
-          const float *hc = Hn + (size_t)jr * sj;
-          const float *yr = Ys + (size_t)i * c;
-          for (int l = 0; l < c; l++) s += yr[l] * hc[l];
-        }
-        stf<TC>(Cn, (size_t)i * r + jr, s);
-        sq += s * s;
-      }
-      part[g0 * r + jr] = sq;
-    }
+    const int ln = tid & 63, l16 = ln & 15, lk = ln >> 4;
+    mfma_gemm_tiles_f32<NW>(
+        b, r, c,
+        [&](int i, int l) { return (i < b && l < c) ? YFP[(size_t)i * D + l] : 0.f; },
+        [&](int l, int jr) { return (l < c && jr < kplus) ? Hn[(size_t)jr * sj + l] : 0.f; },
+        [&](int i0, int j0, mf32x4 acc) {
+          const int jr = j0 + l16;
+          float sq = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const int i = i0 + 4 * lk + v;
+            if (i < b && jr < r) stf<TC>(Cn, (size_t)i * r + jr, acc[v]);
+            sq += acc[v] * acc[v];  // zero for rows past b
+          }
+          sq += __shfl_xor(sq, 16);
+          sq += __shfl_xor(sq, 32);
+          if (lk == 0 && jr < r) sqp[(i0 >> 4) * r + jr] = sq;
+        });
   }
   __syncthreads();
   // sigma = column norms of the stored coordinates: rewritten old rows
@@ -735,7 +692,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     if (tid < kplus) {
       const float *hc = Hn + (size_t)tid * sj;
       for (int l = 0; l < k; l++) s2 += (tau[l] * hc[l]) * (tau[l] * hc[l]);
-      for (int g = 0; g < ngrp; g++) s2 += part[g * r + tid];
+      for (int mt = 0; mt < (b + 15) / 16; mt++) s2 += sqp[mt * r + tid];
     }
     X.sig[(size_t)u * r + tid] = sqrtf(s2);
   }
