@@ -235,6 +235,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   const int kplus = (r < c) ? r : c;
   const int sj = fold_sj(c);
   const FoldLds lay = fold_lds(k, b, r);
+  constexpr int NW = NTF / 64;  // wavefronts
 
   float *tau = smem + lay.big;
   float *sv = tau + D;
@@ -268,6 +269,11 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     }
   }
   constexpr int NGR = NTF / 16;  // 16-lane row groups
+  // When k + b >= d the residual basis has p = d - k columns: it is any
+  // orthonormal basis of the complement of B (the residual rows lie in it),
+  // so it comes from the QR of B alone and E is not needed.
+  const bool cmpl = (k + b >= D);
+  const int nref = cmpl ? k : c;  // reflectors that define P
   float f[NR][8];
 #pragma unroll
   for (int qq = 0; qq < NR; qq++) {
@@ -282,30 +288,45 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       for (int t = 0; t < 8; t++) f[qq][t] = 0.f;
     }
   }
+  if (cmpl) {
+    // the rows of F go to LDS rows k .. k+b-1 (free in this case): both of
+    // their products, F B here and F P below, run on matrix cores
+#pragma unroll
+    for (int qq = 0; qq < NR; qq++) {
+      const int i = grp + NGR * qq;
+      if (i < b) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) A[(size_t)(k + i) * LDA + lane * 8 + t] = f[qq][t];
+      }
+    }
+  }
   __syncthreads();
-  // When k + b >= d the residual basis has p = d - k columns: it is any
-  // orthonormal basis of the complement of B (the residual rows lie in it),
-  // so it comes from the QR of B alone and E is not needed.
-  const bool cmpl = (k + b >= D);
-  const int nref = cmpl ? k : c;  // reflectors that define P
-  // Y = F B and E = F - Y B^T; then once more E <- E - (E B) B^T
-  for (int pass = 0; pass < (cmpl ? 1 : 2); pass++) {
-    for (int j = 0; j < k; j++) {
-      float bj[8];
+  if (cmpl) {
+    // Y = F B
+    mfma_gemm_f32<NW>(
+        b, k, D, [&](int i, int d) { return i < b ? A[(size_t)(k + i) * LDA + d] : 0.f; },
+        [&](int d, int j) { return j < k ? A[(size_t)j * LDA + d] : 0.f; },
+        [&](int i, int j, float v) {
+          if (i < b && j < k) YFP[(size_t)i * D + j] = v;
+        });
+  } else {
+    // Y = F B and E = F - Y B^T; then once more E <- E - (E B) B^T
+    for (int pass = 0; pass < 2; pass++) {
+      for (int j = 0; j < k; j++) {
+        float bj[8];
 #pragma unroll
-      for (int t = 0; t < 8; t++) bj[t] = A[j * LDA + lane * 8 + t];
+        for (int t = 0; t < 8; t++) bj[t] = A[j * LDA + lane * 8 + t];
 #pragma unroll
-      for (int qq = 0; qq < NR; qq++) {
-        float s = 0.f;
+        for (int qq = 0; qq < NR; qq++) {
+          float s = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; t++) s += f[qq][t] * bj[t];
-        s = sum16(s);
-        if (!cmpl) {
+          for (int t = 0; t < 8; t++) s += f[qq][t] * bj[t];
+          s = sum16(s);
 #pragma unroll
           for (int t = 0; t < 8; t++) f[qq][t] -= s * bj[t];
+          const int i = grp + NGR * qq;
+          if (pass == 0 && lane == 0 && i < b) YFP[i * D + j] = s;
         }
-        const int i = grp + NGR * qq;
-        if (pass == 0 && lane == 0 && i < b) YFP[i * D + j] = s;
       }
     }
   }
@@ -380,22 +401,14 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       for (int e = 0; e < 8; e++) dst[e] = float4{x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]};
     }
     if (cmpl) {
-      // F P from the rows of F still in registers (16 lanes per row)
+      // F P, F from LDS rows k .. k+b-1 (the reflectors use rows < k)
       __syncthreads();  // P is complete
-      for (int col = 0; col < p; col++) {
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; t++) pv[t] = Pg[(size_t)col * D + lane * 8 + t];
-#pragma unroll
-        for (int qq = 0; qq < NR; qq++) {
-          float s = 0.f;
-#pragma unroll
-          for (int t = 0; t < 8; t++) s += f[qq][t] * pv[t];
-          s = sum16(s);
-          const int i = grp + NGR * qq;
-          if (lane == 0 && i < b) YFP[i * D + k + col] = s;
-        }
-      }
+      mfma_gemm_f32<NW>(
+          b, p, D, [&](int i, int d) { return i < b ? A[(size_t)(k + i) * LDA + d] : 0.f; },
+          [&](int d, int col) { return col < p ? Pg[(size_t)col * D + d] : 0.f; },
+          [&](int i, int col, float v) {
+            if (i < b && col < p) YFP[(size_t)i * D + k + col] = v;
+          });
     }
   }
   __syncthreads();
@@ -528,7 +541,6 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   __syncthreads();
 
   // The products below run on matrix cores (fp32, the Gram matrices fp64).
-  constexpr int NW = NTF / 64;
   // B+ = [B P] H_r into the second region (rows j' x D, stride LDA)
   float *Bp = smem + (size_t)c * sj;
   mfma_gemm_f32<NW>(
