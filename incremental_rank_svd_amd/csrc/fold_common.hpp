@@ -246,105 +246,249 @@ __device__ __forceinline__ void mfma_gemm_f32(int M, int N, int K, FA fa, FB fb,
   });
 }
 
-// Cyclic sweeps of one-sided Jacobi over the c columns of J (column stride
-// sj; LP lanes per column pair, lane o holding the contiguous rows
-// o * 4NQ .. o * 4NQ + 4NQ - 1; rows past the column length are zero) without
-// accumulating the rotations: on convergence the columns are mutually
-// orthogonal (J V with V orthogonal). A lane group owns one pair of the
-// parallel round-robin order per round; cosines come from fp64 dot products.
-// The squared column norms (fp64, in nrm) are measured at the start of every
-// sweep and carried through each rotation by its exact effect on the two
-// norms, so a pair costs one dot product. A pair is rotated while its cosine
-// exceeds tol and neither column is negligible (squared norm <= negl:
-// rounding noise of the matrix). Stops after a sweep without rotation or at
-// SWEEP_CAP. (Taking the early sweeps' dot products in fp32 was tried: the
-// sweeps it adds cost more than it saves.)
+// One-sided Jacobi over the c columns of J (column stride sj; LP lanes per
+// column pair, lane o holding the contiguous rows o * 4NQ .. o * 4NQ + 4NQ - 1;
+// rows past the column length are zero) without accumulating the rotations:
+// on convergence the columns are mutually orthogonal (J V with V orthogonal).
+// Cosines come from fp64 dot products. The squared column norms (fp64, in
+// nrm) are measured at the start of every sweep and carried through each
+// rotation by its exact effect on the two norms, so a pair costs one dot
+// product. A pair is rotated while its cosine exceeds tol and neither column
+// is negligible (squared norm <= negl: rounding noise of the matrix).
+// (Taking the early sweeps' dot products in fp32 was tried: the sweeps it
+// adds cost more than it saves.)
+
+// rotation of the pair (ci, cj) by the lane group whose lane o is calling;
+// returns 1 if the pair was rotated (the same on all lanes of the group)
+template <int LP, int NQ>
+__device__ __forceinline__ int jacobi_pair(float *J, double *nrm, int sj, int ci, int cj, int o, double tol,
+                                           double negl) {
+  const int rl = 4 * NQ;
+  float4 *zi = (float4 *)(J + (size_t)ci * sj + o * rl);
+  float4 *zj = (float4 *)(J + (size_t)cj * sj + o * rl);
+  float4 xi[NQ], xj[NQ];
+  const double al = nrm[ci], be = nrm[cj];
+  double g[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int e = 0; e < NQ; e++) {
+    xi[e] = zi[e];
+    xj[e] = zj[e];
+  }
+#pragma unroll
+  for (int e = 0; e < NQ; e++) {
+    g[0] = fma((double)xi[e].x, (double)xj[e].x, g[0]);
+    g[1] = fma((double)xi[e].y, (double)xj[e].y, g[1]);
+    g[2] = fma((double)xi[e].z, (double)xj[e].z, g[2]);
+    g[3] = fma((double)xi[e].w, (double)xj[e].w, g[3]);
+  }
+  const double ga = group_sum_d<LP>((g[0] + g[1]) + (g[2] + g[3]));
+  if (!(al > negl && be > negl && ga * ga > tol * tol * (al * be))) return 0;
+  // The rotation only has to be exact (cs^2 + sn^2 = 1 to rounding), not its
+  // angle: a slightly different angle leaves a cosine the next sweep removes.
+  // So the hardware reciprocal and reciprocal square root (about 1 ulp) take
+  // the place of correctly rounded ones.
+  const float zeta = (float)(be - al) * __builtin_amdgcn_rcpf((float)(2.0 * ga));
+  const float az = fabsf(zeta);
+  float t = __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.f)));
+  t = copysignf(t, zeta);
+  const float cs = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
+  const float sn = cs * t;
+#pragma unroll
+  for (int e = 0; e < NQ; e++) {
+    const float4 u0 = xi[e], u1 = xj[e];
+    zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z, cs * u0.w - sn * u1.w};
+    zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z, sn * u0.w + cs * u1.w};
+  }
+  if (o == 0) {
+    const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
+    nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
+    nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
+  }
+  return 1;
+}
+
+// squared column norms in fp64 (lane groups take the columns in turn)
 template <int NTC, int LP, int NQ>
-__device__ __forceinline__ void jacobi_columns(float *J, double *nrm, int sj, int c, double tol, double negl,
-                                               int &sweep, bool &conv) {
+__device__ __forceinline__ void jacobi_norms(const float *J, double *nrm, int sj, int c) {
+  const int tid = threadIdx.x, o = tid % LP, gid = tid / LP;
+  for (int col = gid; col < c; col += NTC / LP) {
+    const float4 *zc = (const float4 *)(J + (size_t)col * sj + o * 4 * NQ);
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int e = 0; e < NQ; e++) {
+      const float4 x = zc[e];
+      s0 = fma((double)x.x, (double)x.x, s0);
+      s1 = fma((double)x.y, (double)x.y, s1);
+      s0 = fma((double)x.z, (double)x.z, s0);
+      s1 = fma((double)x.w, (double)x.w, s1);
+    }
+    const double sn2 = group_sum_d<LP>(s0 + s1);
+    if (o == 0) nrm[col] = sn2;
+  }
+}
+
+// workgroup sum of one int per thread (red: one LDS int, free on entry and
+// on return); every thread gets the sum
+template <int NTC>
+__device__ __forceinline__ int block_sum_int(int v, int *red) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (threadIdx.x == 0) *red = 0;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) atomicAdd(red, v);
+  __syncthreads();
+  const int s = *red;
+  __syncthreads();
+  return s;
+}
+
+// One cyclic sweep in the parallel round-robin order (a lane group owns one
+// pair per round, one barrier per round); returns the number of rotations.
+template <int NTC, int LP, int NQ>
+__device__ __forceinline__ int jacobi_sweep(float *J, double *nrm, int sj, int c, double tol, double negl,
+                                            int *red) {
   constexpr int NG = NTC / LP;  // lane groups; c <= 2 NG, so a group owns at most one pair per round
   const int tid = threadIdx.x, o = tid % LP, gid = tid / LP;
   const int c2 = c + (c & 1), mdl = c2 - 1;
-  const int rl = 4 * NQ;
   const bool has_pair = gid < c2 / 2;
-  while (!conv && sweep < SWEEP_CAP) {
-    sweep++;
-    int rot = 0;
-    for (int col = gid; col < c; col += NG) {
-      const float4 *zc = (const float4 *)(J + (size_t)col * sj + o * rl);
-      double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-      for (int e = 0; e < NQ; e++) {
-        const float4 x = zc[e];
-        s0 = fma((double)x.x, (double)x.x, s0);
-        s1 = fma((double)x.y, (double)x.y, s1);
-        s0 = fma((double)x.z, (double)x.z, s0);
-        s1 = fma((double)x.w, (double)x.w, s1);
-      }
-      const double sn2 = group_sum_d<LP>(s0 + s1);
-      if (o == 0) nrm[col] = sn2;
+  jacobi_norms<NTC, LP, NQ>(J, nrm, sj, c);
+  __syncthreads();
+  int rot = 0;
+  // round-robin players of this group's pair, advanced by one each round
+  // (the order of rr_pair without its two modulo operations per round)
+  int pa = gid == 0 ? 0 : gid, pb = gid == 0 ? c2 - 1 : mdl - gid;
+  for (int rnd = 0; rnd < c2 - 1; rnd++) {
+    const int ci = pa < pb ? pa : pb, cj = pa < pb ? pb : pa;
+    if (has_pair && cj < c) rot += jacobi_pair<LP, NQ>(J, nrm, sj, ci, cj, o, tol, negl);
+    if (gid == 0) {
+      pa++;
+    } else {
+      pa = (pa + 1 == mdl) ? 0 : pa + 1;
+      pb = (pb + 1 == mdl) ? 0 : pb + 1;
     }
     __syncthreads();
-    // round-robin players of this group's pair, advanced by one each round
-    // (the order of rr_pair without its two modulo operations per round)
-    int pa = gid == 0 ? 0 : gid, pb = gid == 0 ? c2 - 1 : mdl - gid;
-    for (int rnd = 0; rnd < c2 - 1; rnd++) {
-      const int ci = pa < pb ? pa : pb, cj = pa < pb ? pb : pa;
-      if (has_pair && cj < c) {
-        float4 *zi = (float4 *)(J + (size_t)ci * sj + o * rl);
-        float4 *zj = (float4 *)(J + (size_t)cj * sj + o * rl);
-        float4 xi[NQ], xj[NQ];
-        const double al = nrm[ci], be = nrm[cj];
-        double g[4] = {0.0, 0.0, 0.0, 0.0};
+  }
+  return block_sum_int<NTC>(o == 0 ? rot : 0, red);
+}
+
+// round of the parallel round-robin order (jacobi_sweep) in which the pair
+// i < j meets: player c2 - 1 meets player rnd in round rnd; otherwise the
+// players of round rnd sum to 2 rnd modulo the odd c2 - 1
+__device__ __forceinline__ int rr_round(int i, int j, int c2) {
+  const int mdl = c2 - 1;
+  if (j == mdl) return i;
+  return (int)(((unsigned)(i + j) * (unsigned)((mdl + 1) / 2)) % (unsigned)mdl);
+}
+
+// The convergence test of a sweep without its sweep: the Gram matrix of the
+// columns in fp64 on matrix cores (the tiles of one triangle, rows padded to
+// 32 NQ with zeros), after measuring the norms afresh. Every pair i < j whose
+// cosine exceeds tol (neither column negligible) sets bit j of row i of
+// flags (c rows of ceil(c / 32) words) and the bit of its round-robin round
+// in rmask (4 words). Returns the number of such pairs: a sweep from this
+// state would rotate exactly these pairs if it met them first, and none if
+// there are none.
+template <int NTC, int LP, int NQ>
+__device__ __forceinline__ int jacobi_flags(const float *J, double *nrm, int sj, int c, double tol, double negl,
+                                            uint32_t *flags, uint32_t *rmask, int *red) {
+  constexpr int NW = NTC / 64;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l16 = ln & 15, lk = ln >> 4;
+  const int W = (c + 31) >> 5, c2 = c + (c & 1);
+  jacobi_norms<NTC, LP, NQ>(J, nrm, sj, c);
+  for (int idx = tid; idx < c * W; idx += NTC) flags[idx] = 0u;
+  if (tid < 4) rmask[tid] = 0u;
+  __syncthreads();
+  int n = 0;
+  const int tk = (c + 15) >> 4;
+  for (int t = wv; t < tk * (tk + 1) / 2; t += NW) {
+    int tj, ti;
+    tri_index(t, tj, ti);  // ti <= tj
+    const int ia = 16 * ti + l16, jb = 16 * tj + l16;
+    const float *ca = J + (size_t)(ia < c ? ia : 0) * sj, *cb = J + (size_t)(jb < c ? jb : 0) * sj;
+    const bool va = ia < c, vb = jb < c;
+    mf64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    for (int k0 = 0; k0 < 32 * NQ; k0 += 16) {
+      double x[4], y[4];
 #pragma unroll
-        for (int e = 0; e < NQ; e++) {
-          xi[e] = zi[e];
-          xj[e] = zj[e];
-        }
+      for (int z = 0; z < 4; z++) {
+        x[z] = va ? (double)ca[k0 + 4 * z + lk] : 0.0;
+        y[z] = vb ? (double)cb[k0 + 4 * z + lk] : 0.0;
+      }
 #pragma unroll
-        for (int e = 0; e < NQ; e++) {
-          g[0] = fma((double)xi[e].x, (double)xj[e].x, g[0]);
-          g[1] = fma((double)xi[e].y, (double)xj[e].y, g[1]);
-          g[2] = fma((double)xi[e].z, (double)xj[e].z, g[2]);
-          g[3] = fma((double)xi[e].w, (double)xj[e].w, g[3]);
-        }
-        const double ga = group_sum_d<LP>((g[0] + g[1]) + (g[2] + g[3]));
-        if (al > negl && be > negl && ga * ga > tol * tol * (al * be)) {
-          // The rotation only has to be exact (cs^2 + sn^2 = 1 to rounding),
-          // not its angle: a slightly different angle leaves a cosine the next
-          // sweep removes. So the hardware reciprocal and reciprocal square
-          // root (about 1 ulp) take the place of correctly rounded ones.
-          const float zeta = (float)(be - al) * __builtin_amdgcn_rcpf((float)(2.0 * ga));
-          const float az = fabsf(zeta);
-          float t = __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.f)));
-          t = copysignf(t, zeta);
-          const float cs = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
-          const float sn = cs * t;
+      for (int z = 0; z < 4; z++) acc = mfma4_f64(x[z], y[z], acc);
+    }
 #pragma unroll
-          for (int e = 0; e < NQ; e++) {
-            const float4 u0 = xi[e], u1 = xj[e];
-            zi[e] = float4{cs * u0.x - sn * u1.x, cs * u0.y - sn * u1.y, cs * u0.z - sn * u1.z,
-                           cs * u0.w - sn * u1.w};
-            zj[e] = float4{sn * u0.x + cs * u1.x, sn * u0.y + cs * u1.y, sn * u0.z + cs * u1.z,
-                           sn * u0.w + cs * u1.w};
-          }
-          if (o == 0) {
-            const double c_ = cs, s_ = sn, cg = 2.0 * c_ * s_ * ga;
-            nrm[ci] = fmax(c_ * c_ * al - cg + s_ * s_ * be, 0.0);
-            nrm[cj] = fmax(s_ * s_ * al + cg + c_ * c_ * be, 0.0);
-          }
-          rot = 1;
+    for (int v = 0; v < 4; v++) {
+      const int i = 16 * ti + lk + 4 * v, j = jb;  // fp64 accumulator layout
+      if (i < j && j < c) {
+        const double g = acc[v], al = nrm[i], be = nrm[j];
+        if (al > negl && be > negl && g * g > tol * tol * (al * be)) {
+          atomicOr(&flags[i * W + (j >> 5)], 1u << (j & 31));
+          const int rnd = rr_round(i, j, c2);
+          atomicOr(&rmask[rnd >> 5], 1u << (rnd & 31));
+          n++;
         }
       }
+    }
+  }
+  return block_sum_int<NTC>(n, red);
+}
+
+// Rotates the flagged pairs: the rounds of the round-robin order that hold a
+// flagged pair, in order, each lane group rotating its pair of the round if
+// that pair is flagged (the rounds of a sweep, restricted to these pairs).
+template <int NTC, int LP, int NQ>
+__device__ __forceinline__ void jacobi_targeted(float *J, double *nrm, int sj, int c, double tol, double negl,
+                                                const uint32_t *flags, const uint32_t *rmask) {
+  const int tid = threadIdx.x, o = tid % LP, gid = tid / LP;
+  const int W = (c + 31) >> 5, c2 = c + (c & 1), mdl = c2 - 1;
+  const bool has_pair = gid < c2 / 2;
+  for (int w = 0; w < 4; w++) {
+    uint32_t m = rmask[w];  // the same on every thread
+    while (m) {
+      const int rnd = 32 * w + __builtin_ctz(m);
+      m &= m - 1;
+      int pa, pb;
       if (gid == 0) {
-        pa++;
+        pa = rnd;
+        pb = mdl;
       } else {
-        pa = (pa + 1 == mdl) ? 0 : pa + 1;
-        pb = (pb + 1 == mdl) ? 0 : pb + 1;
+        pa = (rnd + gid) % mdl;
+        pb = (rnd - gid + mdl) % mdl;
       }
+      const int ci = pa < pb ? pa : pb, cj = pa < pb ? pb : pa;
+      if (has_pair && cj < c && ((flags[ci * W + (cj >> 5)] >> (cj & 31)) & 1u))
+        jacobi_pair<LP, NQ>(J, nrm, sj, ci, cj, o, tol, negl);
       __syncthreads();
     }
-    conv = !__syncthreads_or(rot);
+  }
+}
+
+// Sweeps until one rotates nothing, or, once a sweep rotates few pairs (at
+// most 4c), until the Gram test finds nothing to rotate: after such a sweep,
+// the pairs the test flags are rotated directly (jacobi_targeted) and the
+// test repeated, at most four times before whole sweeps resume. sweep counts
+// whole sweeps and direct passes; conv is false if SWEEP_CAP was reached.
+// flags: c * ceil(c/32) words, rmask: 4 words, red: one int.
+template <int NTC, int LP, int NQ>
+__device__ __forceinline__ void jacobi_columns(float *J, double *nrm, int sj, int c, double tol, double negl,
+                                               int &sweep, bool &conv, uint32_t *flags, uint32_t *rmask,
+                                               int *red) {
+  while (!conv && sweep < SWEEP_CAP) {
+    sweep++;
+    const int nrot = jacobi_sweep<NTC, LP, NQ>(J, nrm, sj, c, tol, negl, red);
+    if (nrot == 0) {
+      conv = true;
+      break;
+    }
+    if (nrot > 4 * c) continue;
+    for (int pass = 0; pass < 4 && !conv && sweep < SWEEP_CAP; pass++) {
+      if (jacobi_flags<NTC, LP, NQ>(J, nrm, sj, c, tol, negl, flags, rmask, red) == 0) {
+        conv = true;
+        break;
+      }
+      sweep++;
+      jacobi_targeted<NTC, LP, NQ>(J, nrm, sj, c, tol, negl, flags, rmask);
+    }
   }
 }
 

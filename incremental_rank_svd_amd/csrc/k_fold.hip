@@ -68,8 +68,8 @@ __host__ __device__ inline FoldLds fold_lds(int k, int b, int r) {
 
 template <int NQ>
 __device__ __forceinline__ void run_jacobi(float *J, double *nrm, int sj, int c, double tol, double negl,
-                                           int &sweep, bool &conv) {
-  jacobi_columns<NTF, LPJ, NQ>(J, nrm, sj, c, tol, negl, sweep, conv);
+                                           int &sweep, bool &conv, uint32_t *flags, uint32_t *rmask, int *red) {
+  jacobi_columns<NTF, LPJ, NQ>(J, nrm, sj, c, tol, negl, sweep, conv, flags, rmask, red);
 }
 
 // sum of a[e] * b[e] over N entries in four independent accumulation chains
@@ -444,11 +444,16 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
     __syncthreads();  // part is reused below
     int sweep = 0;
     bool conv = (c < 2);
+    // Jacobi scratch: the pair flags in tau .. perm (dead until phase D, 4 D
+    // words >= c ceil(c/32)), the round mask and a counter in part
+    uint32_t *flags = (uint32_t *)tau;
+    uint32_t *rmask = (uint32_t *)part;
+    int *red = (int *)(part + 4);
     switch (fold_nq(c)) {
-      case 1: run_jacobi<1>(J, nrm, sj, c, tol, negl, sweep, conv); break;
-      case 2: run_jacobi<2>(J, nrm, sj, c, tol, negl, sweep, conv); break;
-      case 3: run_jacobi<3>(J, nrm, sj, c, tol, negl, sweep, conv); break;
-      default: run_jacobi<4>(J, nrm, sj, c, tol, negl, sweep, conv); break;
+      case 1: run_jacobi<1>(J, nrm, sj, c, tol, negl, sweep, conv, flags, rmask, red); break;
+      case 2: run_jacobi<2>(J, nrm, sj, c, tol, negl, sweep, conv, flags, rmask, red); break;
+      case 3: run_jacobi<3>(J, nrm, sj, c, tol, negl, sweep, conv, flags, rmask, red); break;
+      default: run_jacobi<4>(J, nrm, sj, c, tol, negl, sweep, conv, flags, rmask, red); break;
     }
     if (tid == 0) {
       if (!conv) atomicOr(a.status, FLAG_SWEEP_CAP);
