@@ -55,7 +55,9 @@ __host__ __device__ inline FoldLds fold_lds(int k, int b, int r) {
   const int m = k + b, c = k + p;
   const int kp = (r < c) ? r : c;
   const int sj = fold_sj(c);
-  const int a = m * LDA;                   // [B | E^T] as rows
+  // [B | E^T] as rows; when k + b >= d, B and then the projector I - B^T B
+  // in rows 0 .. d-1 and F in rows d .. d+b-1
+  const int a = (k + b >= D ? D + b : m) * LDA;
   const int h = c * sj;                    // R^T / H
   const int bp = kp * (LDA > sj ? LDA : sj);  // B+ staging (stride LDA), then H_r G (stride sj)
   int big = a;
@@ -288,15 +290,16 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       for (int t = 0; t < 8; t++) f[qq][t] = 0.f;
     }
   }
+  // F's rows in LDS rows d .. d+b-1 when k + b >= d (both of their products,
+  // F B here and F P below, run on matrix cores)
+  float *Fs = A + (size_t)D * LDA;
   if (cmpl) {
-    // the rows of F go to LDS rows k .. k+b-1 (free in this case): both of
-    // their products, F B here and F P below, run on matrix cores
 #pragma unroll
     for (int qq = 0; qq < NR; qq++) {
       const int i = grp + NGR * qq;
       if (i < b) {
 #pragma unroll
-        for (int t = 0; t < 8; t++) A[(size_t)(k + i) * LDA + lane * 8 + t] = f[qq][t];
+        for (int t = 0; t < 8; t++) Fs[(size_t)i * LDA + lane * 8 + t] = f[qq][t];
       }
     }
   }
@@ -304,7 +307,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   if (cmpl) {
     // Y = F B
     mfma_gemm_f32<NW>(
-        b, k, D, [&](int i, int d) { return i < b ? A[(size_t)(k + i) * LDA + d] : 0.f; },
+        b, k, D, [&](int i, int d) { return i < b ? Fs[(size_t)i * LDA + d] : 0.f; },
         [&](int d, int j) { return j < k ? A[(size_t)j * LDA + d] : 0.f; },
         [&](int i, int j, float v) {
           if (i < b && j < k) YFP[(size_t)i * D + j] = v;
@@ -342,7 +345,113 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   }
   __syncthreads();
 
-  if (p > 0) {
+  if (p > 0 && cmpl && p < k) {
+    // P = an orthonormal basis of the complement of B (p = d - k < k): pivoted
+    // Cholesky of the projector M = I - B^T B, p steps (fewer than the k
+    // reflectors of a QR of B), M = G G^T. Since
+    // G G^T = P^T P for any such basis, the columns of G are one: g_s is row
+    // s of P. Step s pivots on the largest remaining diagonal (lowest index
+    // on ties), which is at least 1/d in exact arithmetic.
+    float *M = A;  // d rows, stride LDA (B's rows are dead: Y = F B is done)
+    {
+      // M in fp64 on matrix cores (B from memory, a tile's operands loaded
+      // before its products; one triangle of tiles, mirrored), rounded to fp32
+      const int wv = tid >> 6, ln = tid & 63, l16 = ln & 15, lk = ln >> 4;
+      constexpr int TD = D / 16;
+      for (int t = wv; t < TD * (TD + 1) / 2; t += NW) {
+        int tj, ti;
+        tri_index(t, tj, ti);  // ti <= tj
+        const int ia = 16 * ti + l16, jb = 16 * tj + l16;
+        float x[D / 4], y[D / 4];
+#pragma unroll
+        for (int z = 0; z < D / 4; z++) {
+          const int l = 4 * z + lk;
+          x[z] = l < k ? Bt[(size_t)l * D + ia] : 0.f;
+          y[z] = l < k ? Bt[(size_t)l * D + jb] : 0.f;
+        }
+        mf64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int z = 0; z < D / 4; z++)
+          if (4 * z < k) acc = mfma4_f64((double)x[z], (double)y[z], acc);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const int i = 16 * ti + lk + 4 * v, j = jb;  // fp64 accumulator layout
+          if (i <= j) {
+            const float mv = (float)((i == j ? 1.0 : 0.0) - acc[v]);
+            M[(size_t)i * LDA + j] = mv;
+            M[(size_t)j * LDA + i] = mv;
+          }
+        }
+      }
+    }
+    // indices not yet pivots: a 128-bit mask, the same in every thread
+    uint32_t am[4] = {~0u, ~0u, ~0u, ~0u};
+    auto active = [&](int i) -> bool {
+      const uint32_t w = i < 64 ? (i < 32 ? am[0] : am[1]) : (i < 96 ? am[2] : am[3]);
+      return (w >> (i & 31)) & 1u;
+    };
+    float *g = sv;
+    __syncthreads();
+    for (int st = 0; st < p; st++) {
+      if (tid < 64) {
+        float bv = -1.f;
+        int bi = 0;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int i = tid + 64 * h;
+          const float dv = active(i) ? M[(size_t)i * LDA + i] : -1.f;
+          if (dv > bv) {
+            bv = dv;
+            bi = i;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int oi = __shfl_xor(bi, off);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (tid == 0) {
+          ((int *)part)[0] = bi;
+          part[1] = bv;
+        }
+      }
+      __syncthreads();
+      const int piv = ((const int *)part)[0];
+      if (tid < D) {
+        const float rs = 1.f / sqrtf(fmaxf(part[1], 1e-30f));
+        const float gv = active(tid) ? M[(size_t)tid * LDA + piv] * rs : 0.f;
+        g[tid] = gv;
+        Pg[(size_t)st * D + tid] = gv;
+      }
+      am[piv >> 5] &= ~(1u << (piv & 31));
+      __syncthreads();
+      // M <- M - g g^T on the columns that are not pivots yet (rows that are
+      // pivots have g = 0, except this step's, which is never read again)
+      {
+        const int j = tid & (D - 1), i0 = tid >> 7;
+        if (active(j)) {
+          const float gj = g[j];
+#pragma unroll 8
+          for (int q = 0; q < D / (NTF / D); q++) {
+            const int i = i0 + (NTF / D) * q;
+            M[(size_t)i * LDA + j] -= g[i] * gj;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // F P, F from LDS rows d .. d+b-1
+    mfma_gemm_f32<NW>(
+        b, p, D, [&](int i, int d) { return i < b ? Fs[(size_t)i * LDA + d] : 0.f; },
+        [&](int d, int col) { return col < p ? Pg[(size_t)col * D + d] : 0.f; },
+        [&](int i, int col, float v) {
+          if (i < b && col < p) YFP[(size_t)i * D + k + col] = v;
+        });
+  } else if (p > 0) {
     // Householder QR of [B | E^T] (column j = LDS row j), c reflectors; of B
     // alone (k reflectors) when P is the complement of B. Each column lives in
     // the registers of one quad (lane q: rows 32q .. 32q + 31); reflector j
@@ -401,10 +510,10 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       for (int e = 0; e < 8; e++) dst[e] = float4{x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]};
     }
     if (cmpl) {
-      // F P, F from LDS rows k .. k+b-1 (the reflectors use rows < k)
+      // F P, F from LDS rows d .. d+b-1
       __syncthreads();  // P is complete
       mfma_gemm_f32<NW>(
-          b, p, D, [&](int i, int d) { return i < b ? A[(size_t)(k + i) * LDA + d] : 0.f; },
+          b, p, D, [&](int i, int d) { return i < b ? Fs[(size_t)i * LDA + d] : 0.f; },
           [&](int d, int col) { return col < p ? Pg[(size_t)col * D + d] : 0.f; },
           [&](int i, int col, float v) {
             if (i < b && col < p) YFP[(size_t)i * D + k + col] = v;
