@@ -131,24 +131,43 @@ def cpu_baseline(w, nunits):
                           cores, dt)}
 
 
+# Peak of the fold core's arithmetic: fp64 and (non-packed) fp32 vector FMAs,
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz. The 157.3 TFLOP/s fp32
+# figure needs packed fp32 instructions, which this build leaves disabled.
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
 def core_flops(k, b, r, sweeps, d=128):
-    """Floating-point operations of one fold core for one unit stream, as the
-    kernel computes it: projection and residual (two passes), Householder QR
-    of [B | E^T] and the residual basis P, the QR of Z when it has more rows
-    than columns, `sweeps` one-sided Jacobi sweeps over c = k + p columns (one
-    fp64 dot product, two fp32 rotations of c-long columns per pair, column
-    norms per sweep), the basis update, the two Gram corrections and the new
-    rows. fp64 and fp32 operations are counted alike."""
+    """Floating-point operations of one fold core for one unit stream, in the
+    order the kernel computes them (an FMA counts as two): projection (Y = F B,
+    and when k + b < d the residual E = F - Y B^T in two passes), the residual
+    basis (Householder QR of [B | E^T] and P; when k + b >= d the complement
+    of B: pivoted Cholesky of I - B^T B if p < k, else a QR of B, and F P),
+    the structured QR of Z (b block rows into the triangle), `sweeps`
+    one-sided Jacobi sweeps over the c = k + p rows of R (per pair one dot
+    product and the rotation of two c-long columns, every pair counted as
+    rotated, plus the column norms; a direct pass over the remaining pairs
+    counts as a sweep), then B+, the two Gram matrices (one triangle each),
+    the basis correction, H_r G and the new rows."""
     p = min(b, d - k)
-    m, c = k + b, k + p
+    c = k + p
     kp = min(r, c)
-    f = 8.0 * b * k * d
-    f += sum(4.0 * (d - j) * max(k + b - j, 0) for j in range(c))
-    f += sum(4.0 * (d - j) for col in range(p) for j in range(k + col + 1))
-    if m > c:
-        f += sum(4.0 * (m - j) * (c - j) for j in range(c))
-    f += sweeps * (c * (c - 1) / 2.0 * 14.0 * c + 2.0 * c * c)
-    f += 2.0 * d * c * kp + kp * kp * (2.0 * d + 2.0 * c) + 2.0 * kp * kp * d + 2.0 * c * kp * kp
+    cmpl = k + b >= d
+    if cmpl:
+        f = 2.0 * b * k * d
+        if p > 0 and p < k:
+            f += d * d * k + sum(2.0 * (d - s) * (d - s) for s in range(p))
+        elif p > 0:
+            f += sum(4.0 * (d - j) * (k - j) for j in range(k))
+            f += sum(4.0 * (d - j) for col in range(p) for j in range(min(k + col + 1, k)))
+        f += 2.0 * b * p * d
+    else:
+        f = 8.0 * b * k * d
+        f += sum(4.0 * (d - j) * max(k + b - j, 0) for j in range(c))
+        f += sum(4.0 * (d - j) for col in range(p) for j in range(k + col + 1))
+    f += sum(4.0 * (b + 1) * (c - j) for j in range(c))
+    f += sweeps * (c * (c - 1) / 2.0 * 8.0 * c + 2.0 * c * c)
+    f += 2.0 * d * c * kp + kp * (kp + 1) / 2.0 * (2.0 * d + 2.0 * c) + 2.0 * kp * kp * d + 2.0 * c * kp * kp
     f += 2.0 * b * c * kp
     return f
 
@@ -374,7 +393,7 @@ def fold_decode_bench(args, w):
     rw_b /= args.steps
     dec_b /= args.steps
     kern = {
-        "k_fold": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": 157.3,
+        "k_fold": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,
                    "unit": "TFLOP/s", "avg_launch_ms": avg["core"], "work_per_launch": core_f,
                    "sweeps": [sw[0], sw[1]]},
         "k_rewrite_mfma": {"bound": "hbm", "achieved": rw_b / (avg["rewrite"] * 1e-3) / 1e9,
