@@ -186,6 +186,10 @@ hipError_t launch_project(const FoldArgs &a, int nunits, int kv_bf16, int coord_
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 // one-shot prefill: QR + Jacobi (k_oneshot_svd), then coordinates and sigma (k_oneshot_coords)
 hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
+// one-shot coordinates and sigma on matrix cores (k_rewrite.hip): bf16 rows and
+// coordinates, ranks multiples of 8
+bool oneshot_coords_mfma_ok(const OneshotArgs &a, int kv_bf16, int coord_bf16);
+hipError_t launch_oneshot_coords_mfma(const OneshotArgs &a, int nunits, hipStream_t s);
 // true when launch_decode can take the appended row itself (nnew = 1)
 bool decode_can_fuse(const DecodeArgs &a);
 // true when the split (matrix-core) decode applies to these counters

@@ -1221,6 +1221,7 @@ hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coo
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (oneshot_coords_mfma_ok(a, kv_bf16, coord_bf16)) return launch_oneshot_coords_mfma(a, nunits, s);
   const int rmin = a.X[0].r < a.X[1].r ? a.X[0].r : a.X[1].r;
   const int rmax = a.X[0].r > a.X[1].r ? a.X[0].r : a.X[1].r;
   const size_t lds2 = sizeof(float) * ((size_t)rmax * (D + 1) + (size_t)oneshot_rows_per_pass(rmin) * D + NT);

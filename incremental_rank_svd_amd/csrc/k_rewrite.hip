@@ -267,6 +267,180 @@ hipError_t launch_rewrite_t(const RewriteArgs &a, int x, dim3 grid, size_t lds, 
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// One-shot prefill coordinates on matrix cores: C[i] = X[i] B^T for all prompt
+// rows of a unit (bf16 rows and coordinates), and sigma = the column norms of
+// what is stored. Page "iS-KV: Online Low-Rank KV Cache Compression via
+// Block-Incremental SVD", section "Prefill Compression" (the history's
+// coordinates in the truncated basis). The rewrite's scheme with the 128
+// input dimensions as K (four K steps) and B^T in place of H_top: B (fp32)
+// enters as three bf16 parts, each wave keeps RG 16-row groups in flight with
+// the next ones loading, and outputs leave through LDS as whole rows. One
+// workgroup per unit stream, so the column sums of squares reduce in a fixed
+// order (lanes, then the four waves).
+// ---------------------------------------------------------------------------
+template <int T, int XK>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_coords_mfma(const OneshotArgs a) {
+  extern __shared__ u32x4_t fr[];
+  constexpr int S = D / 32, RG = row_groups<T>();
+  const Stream &X = a.X[XK];
+  const int r = X.r;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int lrel = ul / (a.batch * a.kvh), rem = ul - lrel * (a.batch * a.kvh);
+  const int bi = rem / a.kvh, hh = rem - bi * a.kvh;
+  const uint16_t *src = (const uint16_t *)a.src[XK] +
+                        (((size_t)bi * a.nl_in + a.lrel0 + lrel) * a.kvh + hh) * (size_t)a.nrows * D;
+  const int kplus = min(min(r, a.nrows), D);
+  const float *Bt = X.Bt + (size_t)u * r * D;
+  // fragment (t, s, part) of lane l: B^T[32s + 8(l/16) + e][16t + l%16], e < 8
+  for (int f = wv; f < T * S; f += NT / 64) {
+    const int t = f / S, s = f - t * S;
+    const int j = 16 * t + (lane & 15);
+    const int kb = 32 * s + 8 * (lane >> 4);
+    uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint16_t p0[2], p1[2], p2[2];
+#pragma unroll
+      for (int z = 0; z < 2; z++) {
+        const float h = (j < kplus) ? Bt[(size_t)j * D + kb + e + z] : 0.f;
+        p0[z] = f2bf(h);
+        const float r1 = h - bf2f(p0[z]);
+        p1[z] = f2bf(r1);
+        p2[z] = f2bf(r1 - bf2f(p1[z]));
+      }
+      w0[e / 2] = (uint32_t)p0[0] | ((uint32_t)p0[1] << 16);
+      w1[e / 2] = (uint32_t)p1[0] | ((uint32_t)p1[1] << 16);
+      w2[e / 2] = (uint32_t)p2[0] | ((uint32_t)p2[1] << 16);
+    }
+    fr[(f * HP + 0) * 64 + lane] = u32x4_t{w0[0], w0[1], w0[2], w0[3]};
+    fr[(f * HP + 1) * 64 + lane] = u32x4_t{w1[0], w1[1], w1[2], w1[3]};
+    fr[(f * HP + 2) * 64 + lane] = u32x4_t{w2[0], w2[1], w2[2], w2[3]};
+  }
+  constexpr int RS = 32 * T + 16, NI = (T + 1) / 2;
+  char *stg = reinterpret_cast<char *>(fr + (size_t)T * S * HP * 64) + wv * 16 * RS;
+  float *sqw = reinterpret_cast<float *>(reinterpret_cast<char *>(fr + (size_t)T * S * HP * 64) + (NT / 64) * 16 * RS);
+  __syncthreads();
+  // prompt rows (16 bytes per lane) and coordinate rows through buffer
+  // resources whose ranges are the unit's rows: rows past nrows read zeros
+  // and are not written
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, a.nrows * D * 2, 0x00020000);
+  uint16_t *C = (uint16_t *)X.C + (size_t)u * X.cstride;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, a.nrows * r * 2, 0x00020000);
+  constexpr uint32_t OUT = 0x80000000u;
+  const int jq = 4 * (lane >> 4);
+  char *stw = stg + (lane & 15) * RS + 2 * jq;
+  uint32_t sl[NI], so[NI];
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    const int off = 1024 * i + 16 * lane, row = off / (2 * r), col = off - row * 2 * r;
+    const bool in = off < 32 * r;
+    sl[i] = in ? row * RS + col : 0;
+    so[i] = in ? (uint32_t)off : OUT;
+  }
+  const int ngroups = (a.nrows + 15) / 16;
+  constexpr int gstride = NT / 64;
+  auto load_groups = [&](int g0, u32x4_t (&cf)[RG][S]) {
+#pragma unroll
+    for (int q = 0; q < RG; q++) {
+      const uint32_t ro = (uint32_t)((g0 + q * gstride) * 16 + (lane & 15)) * (uint32_t)(2 * D) + 16u * (lane >> 4);
+#pragma unroll
+      for (int s = 0; s < S; s++) cf[q][s] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(ro + 64u * s), 0, 0);
+    }
+  };
+  float sq[T][4];
+#pragma unroll
+  for (int t = 0; t < T; t++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) sq[t][v] = 0.f;
+  u32x4_t cf[RG][S], cn[RG][S];
+  if (wv < ngroups) load_groups(wv, cn);
+  for (int g0 = wv; g0 < ngroups; g0 += RG * gstride) {
+#pragma unroll
+    for (int q = 0; q < RG; q++)
+#pragma unroll
+      for (int s = 0; s < S; s++) cf[q][s] = cn[q][s];
+    if (g0 + RG * gstride < ngroups) load_groups(g0 + RG * gstride, cn);
+    u32x2_t ob[RG][T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      f32x4_t acc[RG];
+#pragma unroll
+      for (int q = 0; q < RG; q++) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S; s++) {
+        const u32x4_t *fp = fr + (size_t)((t * S + s) * HP) * 64 + lane;
+#pragma unroll
+        for (int part = 0; part < HP; part++) {
+          const u32x4_t f = fp[64 * part];
+#pragma unroll
+          for (int q = 0; q < RG; q++) acc[q] = mfma_bf16(f, cf[q][s], acc[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < RG; q++) {
+        ob[q][t] = u32x2_t{pack_bf16(acc[q][0], acc[q][1]), pack_bf16(acc[q][2], acc[q][3])};
+        // squares of the stored (rounded) values; rows past nrows are zero
+        const float v0 = __uint_as_float(ob[q][t][0] << 16), v1 = __uint_as_float(ob[q][t][0] & 0xffff0000u);
+        const float v2 = __uint_as_float(ob[q][t][1] << 16), v3 = __uint_as_float(ob[q][t][1] & 0xffff0000u);
+        sq[t][0] += v0 * v0;
+        sq[t][1] += v1 * v1;
+        sq[t][2] += v2 * v2;
+        sq[t][3] += v3 * v3;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < RG; q++) {
+#pragma unroll
+      for (int t = 0; t < T; t++) *reinterpret_cast<u32x2_t *>(stw + 32 * t) = ob[q][t];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint32_t go = (uint32_t)(g0 + q * gstride) * (uint32_t)(32 * r);
+#pragma unroll
+      for (int i = 0; i < NI; i++)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t *>(stg + sl[i]), rc,
+                                               (int)(go + so[i]), 0, 0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+  }
+  // column sums of squares: over the 16 rows of each lane group (fixed
+  // butterfly), then over the four waves in order
+#pragma unroll
+  for (int t = 0; t < T; t++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      float x = sq[t][v];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if ((lane & 15) == 0) sqw[wv * (16 * T) + 16 * t + jq + v] = x;
+    }
+  __syncthreads();
+  if ((int)threadIdx.x < r) {
+    const int j = threadIdx.x;
+    float s2 = 0.f;
+    for (int w = 0; w < NT / 64; w++) s2 += sqw[w * (16 * T) + j];
+    X.sig[(size_t)u * r + j] = (j < kplus) ? sqrtf(s2) : 0.f;
+  }
+}
+
+template <int T>
+hipError_t launch_coords_t(const OneshotArgs &a, int x, int nunits, hipStream_t s) {
+  const size_t lds = (size_t)T * (D / 32) * HP * 64 * 16 + (size_t)(NT / 64) * 16 * (32 * T + 16) +
+                     sizeof(float) * (NT / 64) * 16 * T;
+  const void *f = x == 0 ? (const void *)k_coords_mfma<T, 0> : (const void *)k_coords_mfma<T, 1>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (x == 0)
+    hipLaunchKernelGGL((k_coords_mfma<T, 0>), dim3(nunits), dim3(NT), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_coords_mfma<T, 1>), dim3(nunits), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s) {
@@ -320,6 +494,33 @@ hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipS
     hipLaunchKernelGGL(k_rewrite_vec<float>, grid, dim3(NT), lds, s, a);
   }
   return hipGetLastError();
+}
+
+}  // namespace iskv
+
+namespace iskv {
+
+bool oneshot_coords_mfma_ok(const OneshotArgs &a, int kv_bf16, int coord_bf16) {
+  return kv_bf16 && coord_bf16 && a.X[0].r % 8 == 0 && a.X[1].r % 8 == 0 &&
+         ((size_t)a.nrows + 65536) * D * 2 < ((size_t)1 << 31);
+}
+
+hipError_t launch_oneshot_coords_mfma(const OneshotArgs &a, int nunits, hipStream_t s) {
+  for (int x = 0; x < 2; x++) {
+    hipError_t e;
+    switch ((a.X[x].r + 15) / 16) {
+      case 1: e = launch_coords_t<1>(a, x, nunits, s); break;
+      case 2: e = launch_coords_t<2>(a, x, nunits, s); break;
+      case 3: e = launch_coords_t<3>(a, x, nunits, s); break;
+      case 4: e = launch_coords_t<4>(a, x, nunits, s); break;
+      case 5: e = launch_coords_t<5>(a, x, nunits, s); break;
+      case 6: e = launch_coords_t<6>(a, x, nunits, s); break;
+      case 7: e = launch_coords_t<7>(a, x, nunits, s); break;
+      default: e = launch_coords_t<8>(a, x, nunits, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace iskv
