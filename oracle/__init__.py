@@ -61,7 +61,8 @@ def _bind(lib):
     lib.ora_fold.argtypes = [ctypes.c_int] * 5 + [_D, ctypes.c_int, _D, _D, _D, ctypes.c_int,
                                                   ctypes.c_int, ctypes.POINTER(_FoldInfo)]
     lib.ora_fold.restype = ctypes.c_int
-    lib.ora_run.argtypes = [ctypes.c_int] * 6 + [_D, ctypes.c_int, _D, _D, _D, _I, _D, ctypes.c_int]
+    lib.ora_run.argtypes = [ctypes.c_int] * 6 + [_D, ctypes.c_int, ctypes.c_int, _D, _D, _D, _I, _D,
+                                                 ctypes.c_int]
     lib.ora_run.restype = ctypes.c_int
     lib.ora_reconstruct.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _D, _D,
                                     ctypes.c_int, _D, _D]
@@ -72,6 +73,13 @@ def _bind(lib):
     lib.ora_prefill_oneshot.argtypes = [ctypes.c_int] * 3 + [_D, _D, ctypes.c_int, _D, _D,
                                                               ctypes.POINTER(_FoldInfo)]
     lib.ora_prefill_oneshot.restype = ctypes.c_int
+    lib.ora_store_i8.argtypes = [ctypes.c_int] * 3 + [_D, ctypes.POINTER(ctypes.c_int8), ctypes.c_int, _D]
+    lib.ora_store_i8.restype = None
+    lib.ora_store_u_i8.argtypes = [ctypes.c_int] * 3 + [_D, _D, ctypes.POINTER(ctypes.c_int8), ctypes.c_int, _D]
+    lib.ora_store_u_i8.restype = None
+    lib.ora_fold_i8.argtypes = [ctypes.c_int] * 5 + [_D, ctypes.c_int, _D, _D, _D, ctypes.c_int,
+                                                     ctypes.POINTER(_FoldInfo)]
+    lib.ora_fold_i8.restype = ctypes.c_int
     lib.ora_storage_bytes.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double]
     lib.ora_storage_bytes.restype = ctypes.c_double
     return lib
@@ -150,6 +158,7 @@ class UnitState:
     k: int = 0
     window: list = field(default_factory=list)
     log: list = field(default_factory=list)  # per fold: (k, p, kplus, sweeps, discarded)
+    store: str = "f64"     # "f64", or "i8": C holds int8-stored rows (ora_store_i8)
 
     @classmethod
     def empty(cls, d, b, r, capacity):
@@ -168,8 +177,14 @@ class UnitState:
             grow[: self.C.shape[0]] = self.C
             self.C = grow
         info = _FoldInfo()
-        rc = lib.ora_fold(self.d, self.b, self.r, self.n, self.k, _p(self.C), self.d,
-                          _p(self.sigma), _p(self.Bt), _p(F), mode, porder, ctypes.byref(info))
+        if self.store == "i8":
+            if mode != 0:
+                raise ValueError("int8 coordinate storage is defined for the joint update only")
+            rc = lib.ora_fold_i8(self.d, self.b, self.r, self.n, self.k, _p(self.C), self.d,
+                                 _p(self.sigma), _p(self.Bt), _p(F), porder, ctypes.byref(info))
+        else:
+            rc = lib.ora_fold(self.d, self.b, self.r, self.n, self.k, _p(self.C), self.d,
+                              _p(self.sigma), _p(self.Bt), _p(F), mode, porder, ctypes.byref(info))
         if rc != 0:
             raise OracleError("ora_fold failed: %d" % rc)
         self.log.append((info.k, info.p, info.kplus, info.sweeps, info.discarded))
@@ -211,6 +226,8 @@ class UnitState:
                                      _p(self.Bt), ctypes.byref(info))
         if kp < 0:
             raise OracleError("ora_prefill_oneshot failed: %d" % kp)
+        if self.store == "i8":
+            lib.ora_store_u_i8(N, kp, self.d, _p(self.C), _p(self.sigma), None, 0, None)
         self.log.append((info.k, info.p, info.kplus, info.sweeps, info.discarded))
         self.n = N
         self.k = kp
@@ -259,9 +276,37 @@ def attend(Kt, Vt, q, scale, lib=None):
     return out
 
 
-def run_unit(X, d, b, r, w, prefill=0, mode=0, lib=None):
+def store_i8(C, k, lib=None):
+    """Per-row int8 storage of C's first k columns (ora_store_i8).
+    Returns (stored values, int8 codes, per-row scales)."""
+    lib = lib or load()
+    S = _f64(C).copy()
+    rows, ldc = S.shape
+    Q = np.zeros((rows, ldc), dtype=np.int8)
+    sc = np.zeros(rows)
+    lib.ora_store_i8(rows, k, ldc, _p(S), Q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), ldc, _p(sc))
+    return S, Q, sc
+
+
+def store_u_i8(C, sigma, k, lib=None):
+    """int8 storage of a history C = U Sigma (ora_store_u_i8): U = C Sigma^-1
+    stored per row. Returns (stored C, int8 codes of U, per-row scales of U)."""
+    lib = lib or load()
+    S = _f64(C).copy()
+    rows, ldc = S.shape
+    sg = np.zeros(max(ldc, k))
+    sg[:k] = _f64(sigma)[:k]
+    Q = np.zeros((rows, ldc), dtype=np.int8)
+    sc = np.zeros(rows)
+    lib.ora_store_u_i8(rows, k, ldc, _p(S), _p(sg), Q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), ldc,
+                       _p(sc))
+    return S, Q, sc
+
+
+def run_unit(X, d, b, r, w, prefill=0, mode=0, store="f64", lib=None):
     """Drive one stream through the C driver: prefill rows fold directly, the
-    rest arrive one at a time through the window. Returns a UnitState."""
+    rest arrive one at a time through the window. store="i8" keeps the
+    coordinates as int8 rows with per-row scales. Returns a UnitState."""
     lib = lib or load()
     X = _f64(X)
     N = X.shape[0]
@@ -271,12 +316,12 @@ def run_unit(X, d, b, r, w, prefill=0, mode=0, lib=None):
     counts = np.zeros(3, dtype=np.int32)
     cap = N // b + 1
     log = np.zeros((cap, 5))
-    folds = lib.ora_run(d, b, r, w, N, prefill, _p(X), mode, _p(C), _p(sigma), _p(Bt),
-                        counts.ctypes.data_as(_I), _p(log), cap)
+    folds = lib.ora_run(d, b, r, w, N, prefill, _p(X), mode, 1 if store == "i8" else 0, _p(C),
+                        _p(sigma), _p(Bt), counts.ctypes.data_as(_I), _p(log), cap)
     if folds < 0:
         raise OracleError("ora_run failed: %d" % folds)
     n, e, k = (int(x) for x in counts)
-    st = UnitState(d=d, b=b, r=r, C=C, sigma=sigma, Bt=Bt, n=n, k=k)
+    st = UnitState(d=d, b=b, r=r, C=C, sigma=sigma, Bt=Bt, n=n, k=k, store=store)
     st.window = [row.copy() for row in X[N - e:]]
     st.log = [(int(a), int(p_), int(kp), int(sw), float(ds)) for a, p_, kp, sw, ds in log[:folds]]
     return st

@@ -141,6 +141,13 @@ int ora_singular_values(int m, int c, const double *X, double *sv_sorted, int ma
   return rc;
 }
 
+/* Rank after a fold from rank k (section "Block-Incremental Decoding
+ * Updates": p = min(b, d - k) residual directions, k+ = min(r, k + p)). */
+static int kplus_after(int d, int b, int r, int k) {
+  const int p = (b < d - k) ? b : d - k;
+  return (r < k + p) ? r : k + p;
+}
+
 /* Orthogonalize v (length d) against the rows of `basis` (nb x d) by
  * modified Gram-Schmidt, two passes; returns the norm of the result. */
 static double mgs2(double *v, const double *basis, int nb, int d) {
@@ -402,6 +409,92 @@ out:
 }
 
 /* ------------------------------------------------------------------------ */
+/* Low-bit storage of the history coordinates. The page's "Conclusion" names  */
+/* integration with quantization as the way to cut memory further, and the   */
+/* JoLT abstract on the "Tensor Decomposition of Transformer Key-Value        */
+/* Caches" page keeps its factors in low precision; neither fixes a format.   */
+/* Reading taken here: symmetric int8 codes with one scale per stored row.    */
+/* For row c (columns 0..k-1) with m = max_j |c_j|:                           */
+/*   scale s = m / 127,  code q_j = round-half-even(127 c_j / m)              */
+/* (a zero row has s = 0 and q = 0); the stored value is q_j s, so the row's  */
+/* largest entry keeps its magnitude and every entry moves by at most s / 2.  */
+/* In place: rows 0..rows-1 of C (leading dimension ldc) become their stored  */
+/* values; columns k.. are set to zero. Q (rows x ldq) and scale (rows)       */
+/* receive the codes and scales when they are not NULL.                       */
+/* ------------------------------------------------------------------------ */
+void ora_store_i8(int rows, int k, int ldc, double *C, int8_t *Q, int ldq, double *scale) {
+  for (int i = 0; i < rows; i++) {
+    double *c = C + (size_t)i * ldc;
+    double m = 0.0;
+    for (int j = 0; j < k; j++) m = fabs(c[j]) > m ? fabs(c[j]) : m;
+#ifdef ORA_PLANT_Q8_SCALE128
+    const double levels = 128.0;
+#else
+    const double levels = 127.0;
+#endif
+    const double s = m / levels;
+    for (int j = 0; j < ldc; j++) {
+      double q = 0.0;
+      if (j < k && m > 0.0) {
+        const double x = levels * c[j] / m;
+#if defined(ORA_PLANT_Q8_TRUNC)
+        q = trunc(x);
+#elif defined(ORA_PLANT_Q8_HALFAWAY)
+        q = round(x);
+#else
+        q = nearbyint(x); /* default rounding mode: to nearest, ties to even */
+#endif
+      }
+      if (Q && j < ldq) Q[(size_t)i * ldq + j] = (int8_t)q;
+      c[j] = q * s;
+    }
+    if (scale) scale[i] = s;
+  }
+}
+
+/* int8 storage of a history (rows 0..rows-1 of C = U Sigma, k columns):    */
+/* the stored factor is U = C Sigma^-1, the one the page's equation for U+    */
+/* updates, whose rows have comparable entries (a row of U Sigma inherits the */
+/* power-law decay of sigma, so one scale per row would waste the codes of   */
+/* its small coordinates). Each row of U is stored by ora_store_i8 and C      */
+/* becomes U_stored Sigma. Columns with sigma_j = 0 are zero. Q and scale as  */
+/* in ora_store_i8 (codes and scales of U).                                  */
+void ora_store_u_i8(int rows, int k, int ldc, double *C, const double *sigma, int8_t *Q, int ldq,
+                    double *scale) {
+  for (int i = 0; i < rows; i++) {
+    double *c = C + (size_t)i * ldc;
+    for (int j = 0; j < k; j++)
+#ifdef ORA_PLANT_Q8_STORE_C
+      (void)sigma;
+#else
+      c[j] = sigma[j] > 0.0 ? c[j] / sigma[j] : 0.0;
+#endif
+    ora_store_i8(1, k, ldc, c, Q ? Q + (size_t)i * ldq : NULL, ldq, scale ? scale + i : NULL);
+#ifndef ORA_PLANT_Q8_STORE_C
+    for (int j = 0; j < k; j++) c[j] *= sigma[j];
+#endif
+  }
+}
+
+/* One update with int8 coordinate storage: the fold of the method on the     */
+/* stored history, then every stored row is stored again (ora_store_u_i8      */
+/* with the new sigma): the n old rows after their rotation and the b new     */
+/* rows. Sigma and the basis are the fold's. Rows 0..n-1 of C must hold       */
+/* stored values.                                                            */
+int ora_fold_i8(int d, int b, int r, int n, int k, double *C, int ldc, double *sigma, double *Bt,
+                const double *F, int porder, ora_fold_info *info) {
+  int rc = ora_fold(d, b, r, n, k, C, ldc, sigma, Bt, F, 0, porder, info);
+  if (rc) return rc;
+  const int kplus = info ? info->kplus : kplus_after(d, b, r, k);
+#ifdef ORA_PLANT_Q8_OLDROWS
+  ora_store_u_i8(b, kplus, ldc, C + (size_t)n * ldc, sigma, NULL, 0, NULL);
+#else
+  ora_store_u_i8(n + b, kplus, ldc, C, sigma, NULL, 0, NULL);
+#endif
+  return ORA_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* One-shot prefill (section "Prefill Compression": the prompt's rows are    */
 /* factorised at once by a truncated SVD; key and value protection are not  */
 /* modelled, so every row goes to the history).                              */
@@ -485,11 +578,14 @@ out:
 /*   C (N x d, ldc = d), sigma (d), Bt (d x d), win_first (index into X of   */
 /*   the oldest window row), and counts[3] = {n, e, k}.                      */
 /*   log (optional, 5 doubles per fold): k, p, kplus, sweeps, discarded.     */
+/*   store    : 0 = fp64 coordinates; 1 = int8 rows with per-row scales      */
+/*              (ora_fold_i8; joint mode only), C then holds stored values.  */
 /* Returns the number of folds, or a negative error.                         */
 /* ------------------------------------------------------------------------ */
 int ora_run(int d, int b, int r, int w, int N, int prefill, const double *X, int mode,
-            double *C, double *sigma, double *Bt, int *counts, double *log, int log_cap) {
+            int store, double *C, double *sigma, double *Bt, int *counts, double *log, int log_cap) {
   if (prefill < 0 || prefill % b != 0 || prefill > N) return ORA_ERR_ARG;
+  if (store < 0 || store > 1 || (store == 1 && mode != 0)) return ORA_ERR_ARG;
   int n = 0, k = 0, folds = 0;
   memset(sigma, 0, sizeof(double) * d);
   memset(Bt, 0, sizeof(double) * d * d);
@@ -504,7 +600,8 @@ int ora_run(int d, int b, int r, int w, int N, int prefill, const double *X, int
 #if defined(ORA_PLANT_PREFILL_JOINT)
     int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fs, 0, 0, &info);
 #else
-    int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fs, mode, 0, &info);
+    int rc = store ? ora_fold_i8(d, b, r, n, k, C, d, sigma, Bt, Fs, 0, &info)
+                   : ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fs, mode, 0, &info);
 #endif
     if (rc) return rc;
     if (log && folds < log_cap) {
@@ -519,7 +616,9 @@ int ora_run(int d, int b, int r, int w, int N, int prefill, const double *X, int
   for (int t = prefill; t < N; t++) {
     int e = t + 1 - first;
     if (e >= w + b) {
-      int rc = ora_fold(d, b, r, n, k, C, d, sigma, Bt, X + (size_t)first * d, mode, 0, &info);
+      const double *Fw = X + (size_t)first * d;
+      int rc = store ? ora_fold_i8(d, b, r, n, k, C, d, sigma, Bt, Fw, 0, &info)
+                     : ora_fold(d, b, r, n, k, C, d, sigma, Bt, Fw, mode, 0, &info);
       if (rc) return rc;
       if (log && folds < log_cap) {
         double *lg = log + (size_t)folds * 5;

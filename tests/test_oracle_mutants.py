@@ -34,6 +34,11 @@ PLANTS = [
     "ORA_PLANT_NAIVE_PERM",
     "ORA_PLANT_PREFILL_REVERSED",
     "ORA_PLANT_PREFILL_JOINT",
+    "ORA_PLANT_Q8_TRUNC",
+    "ORA_PLANT_Q8_HALFAWAY",
+    "ORA_PLANT_Q8_SCALE128",
+    "ORA_PLANT_Q8_OLDROWS",
+    "ORA_PLANT_Q8_STORE_C",
 ]
 
 
@@ -41,7 +46,8 @@ def _run_pins(lib_path):
     env = dict(os.environ, ISKV_ORACLE_LIB=lib_path, OMP_NUM_THREADS="1",
                OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-           os.path.join(ROOT, "tests", "test_oracle_pins.py")]
+           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+           os.path.join(ROOT, "tests", "test_oracle_i8.py")]
     p = subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     return p.returncode, p.stdout[-2000:]
 
