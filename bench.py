@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="time the one-shot prompt factorisation of the long-input workload against "
                         "folding the same prompt block by block, print one JSON line and exit")
+    p.add_argument("--coords", choices=("f32", "bf16", "i8"), default=None,
+                   help="stored coordinate type (default: the workload's); i8 = int8 codes of U with "
+                        "one fp32 scale per row")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device-to-device copy and exit (reference for HBM byte counters)")
     return p.parse_args()
@@ -76,12 +79,13 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
-def decode_bytes(U, g, n, e, kK, kV, coord_b, kv_b, appended=0):
+def decode_bytes(U, g, n, e, kK, kV, coord_b, kv_b, appended=0, scale_b=0):
     """Algorithmic HBM bytes of one decode launch over U units: history
-    coordinates of K and V, window rows of K and V (e includes an appended
+    coordinates of K and V (plus scale_b bytes of row scale per history row
+    and kind for int8 storage), window rows of K and V (e includes an appended
     row, read from the caller's buffer), both bases, queries in, outputs out
     (fp32), and the appended K and V rows written to the window ring."""
-    per = (n * (kK + kV) * coord_b + 2 * e * 128 * kv_b + (kK + kV) * 128 * 4
+    per = (n * (kK + kV) * coord_b + 2 * n * scale_b + 2 * e * 128 * kv_b + (kK + kV) * 128 * 4
            + g * 128 * kv_b + g * 128 * 4 + appended * 2 * 128 * kv_b)
     return U * per
 
@@ -172,10 +176,11 @@ def core_flops(k, b, r, sweeps, d=128):
     return f
 
 
-def rewrite_bytes(U, n, k, kp, coord_b):
+def rewrite_bytes(U, n, k, kp, coord_b, scale_b=0):
     """Algorithmic HBM bytes of one rewrite launch for one stream kind: the n
-    stored rows read (k columns) and written (k+ columns), H_top read."""
-    return U * (coord_b * (n * k + n * kp) + 4 * k * kp)
+    stored rows read (k columns) and written (k+ columns), their row scales
+    read and written for int8 storage (scale_b bytes each), H_top read."""
+    return U * (coord_b * (n * k + n * kp) + 2 * n * scale_b + 4 * k * kp)
 
 
 def cpu_model():
@@ -279,7 +284,8 @@ def fold_decode_bench(args, w):
     B, L, Hk, Hq, b, wnd = w.batch, w.layers, w.kv_heads, w.q_heads, w.block, w.window
     U = B * L * Hk
     kv_b = 2 if w.kv_dtype == "bf16" else 4
-    coord_b = 2 if w.coord_dtype == "bf16" else 4
+    coord_b = {"bf16": 2, "f32": 4, "i8": 1}[w.coord_dtype]
+    scale_b = 4 if w.coord_dtype == "i8" else 0  # one fp32 scale per stored row
     kvdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
     nsteps = args.warmup + args.steps
     n_end = w.final_counts()[0]
@@ -387,8 +393,8 @@ def fold_decode_bench(args, w):
     for s in range(args.warmup, nsteps):
         n = n0 + s * b  # history rows before this step's fold
         core_f += U * (core_flops(kK, b, w.rank_k, sw[0]) + core_flops(kV, b, w.rank_v, sw[1]))
-        rw_b += rewrite_bytes(U, n, kK, kK, coord_b) + rewrite_bytes(U, n, kV, kV, coord_b)
-        dec_b += decode_bytes(U, w.group, n + b, wnd, kK, kV, coord_b, kv_b)
+        rw_b += rewrite_bytes(U, n, kK, kK, coord_b, scale_b) + rewrite_bytes(U, n, kV, kV, coord_b, scale_b)
+        dec_b += decode_bytes(U, w.group, n + b, wnd, kK, kV, coord_b, kv_b, scale_b=scale_b)
     core_f /= args.steps
     rw_b /= args.steps
     dec_b /= args.steps
@@ -396,14 +402,15 @@ def fold_decode_bench(args, w):
         "k_fold": {"bound": "alu", "achieved": core_f / (avg["core"] * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,
                    "unit": "TFLOP/s", "avg_launch_ms": avg["core"], "work_per_launch": core_f,
                    "sweeps": [sw[0], sw[1]]},
-        "k_rewrite_mfma": {"bound": "hbm", "achieved": rw_b / (avg["rewrite"] * 1e-3) / 1e9,
+        ("k_rewrite_i8" if scale_b else "k_rewrite_mfma"): {
+                           "bound": "hbm", "achieved": rw_b / (avg["rewrite"] * 1e-3) / 1e9,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_ms": avg["rewrite"],
                            "work_per_launch": rw_b},
         "k_decode_unit": {"bound": "hbm", "achieved": dec_b / (avg["decode"] * 1e-3) / 1e9,
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_ms": avg["decode"],
                           "work_per_launch": dec_b},
     }
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name + ("_i8" if scale_b else ""))
     for name, kr in kern.items():
         kr["frac"] = kr["achieved"] / kr["peak"]
         kr["share_of_step"] = kr["avg_launch_ms"] * 1e-3 / step_s
@@ -421,11 +428,12 @@ def fold_decode_bench(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 storage, f32 compute" if w.kv_dtype == "bf16" else "f32",
+        "dtype": ("int8 U with fp32 row scales, bf16 rows, f32 compute" if scale_b else
+                  "bf16 storage, f32 compute" if w.kv_dtype == "bf16" else "f32"),
         "data": "synthetic (power-law spectrum KV, seeded), resident in HBM",
         "config": {"workload": w.name, "batch": B, "layers": L, "kv_heads": Hk, "q_heads": Hq,
                    "head_dim": 128, "tokens": w.total_tokens, "block": b, "rank_k": w.rank_k,
-                   "rank_v": w.rank_v, "window": wnd,
+                   "rank_v": w.rank_v, "window": wnd, "coords": w.coord_dtype,
                    "step": "one fold round (b = %d new K and V rows per unit, all layers) + one decode "
                            "query per head over all layers; history n = %d -> %d over the warmup and "
                            "timed steps (the run's last fold rounds), window %d" % (b, n0, n_end, wnd)},
@@ -437,7 +445,7 @@ def fold_decode_bench(args, w):
     }
     # decode of one layer per call, as a model's layer loop issues it (after the timed region)
     res["decode_one_layer"] = one_layer_decode(lib, h, Q[-1], out, L, B, Hk, Hq, n_fin, wnd, kK, kV, w.group,
-                                               coord_b, kv_b, stream, sp)
+                                               coord_b, kv_b, stream, sp, scale_b=scale_b)
     print("timed: %d steps, %.1f ms per step" % (args.steps, step_s * 1e3), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_fold_decode(w, n0 + (args.warmup + args.steps // 2) * b,
@@ -445,7 +453,8 @@ def fold_decode_bench(args, w):
     print(json.dumps(res), flush=True)
 
 
-def one_layer_decode(lib, h, q, out, L, B, Hk, Hq, n, e, kK, kV, g, coord_b, kv_b, stream, sp, reps=50):
+def one_layer_decode(lib, h, q, out, L, B, Hk, Hq, n, e, kK, kV, g, coord_b, kv_b, stream, sp, reps=50,
+                     scale_b=0):
     """Median latency of iskv_decode_attn over a single layer (layer 0), the
     call a model's per-layer decode loop makes: B * Hk units, history split
     over several workgroups per unit. q, out: [B, L, Hq, 128] (one layer
@@ -468,7 +477,7 @@ def one_layer_decode(lib, h, q, out, L, B, Hk, Hq, n, e, kK, kV, g, coord_b, kv_
     torch.cuda.synchronize()
     us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1e3
     U1 = B * Hk
-    byts = decode_bytes(U1, g, n, e, kK, kV, coord_b, kv_b)
+    byts = decode_bytes(U1, g, n, e, kK, kV, coord_b, kv_b, scale_b=scale_b)
     return {"units": U1, "n": n, "median_us_with_event_pair": us, "GBps": byts / (us * 1e-6) / 1e9}
 
 
@@ -568,10 +577,13 @@ def main():
 
     import synth
 
+    from dataclasses import replace
+
     w = synth.get_config(args.workload)
     if args.layers:
-        from dataclasses import replace
         w = replace(w, layers=args.layers)
+    if args.coords:
+        w = replace(w, coord_dtype=args.coords)
     if not args.full_run:
         fold_decode_bench(args, w)
         return
@@ -597,7 +609,8 @@ def full_run_bench(args, w):
     U = B * L * Hk
     kvdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
     kv_b = 2 if w.kv_dtype == "bf16" else 4
-    coord_b = 2 if w.coord_dtype == "bf16" else 4
+    coord_b = {"bf16": 2, "f32": 4, "i8": 1}[w.coord_dtype]
+    scale_b = 4 if w.coord_dtype == "i8" else 0
 
     # inputs resident in HBM, token-major so every token's rows are contiguous
     K = synth.kv_rows_torch(w, "K", T, dev)            # [B, L, Hk, T, d]
@@ -657,7 +670,7 @@ def full_run_bench(args, w):
                         e0.record(stream)
                         seg = [e0, 0, 0]
                     if seg is not None:
-                        seg[1] += decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, appended=1)
+                        seg[1] += decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, appended=1, scale_b=scale_b)
                         seg[2] += 1
                 if folds:
                     nseg += 1
@@ -712,7 +725,7 @@ def full_run_bench(args, w):
         evs.append((a0, a1))
     torch.cuda.synchronize()
     final_ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
-    final_bytes = decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b)
+    final_bytes = decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, scale_b=scale_b)
 
     rows_folded = 2 * U * n_final
     traffic = None
@@ -752,7 +765,7 @@ def full_run_bench(args, w):
                      "share_of_step": dec_share},
     }
     res["decode_one_layer"] = one_layer_decode(lib, h, Q[-1], out, L, B, Hk, Hq, n, e, kK, kV, w.group,
-                                               coord_b, kv_b, stream, sp)
+                                               coord_b, kv_b, stream, sp, scale_b=scale_b)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
     print(json.dumps(res), flush=True)

@@ -65,7 +65,16 @@ typedef enum {
 /* Bytes of the library's static device array used by iskv_decode_attn_static. */
 #define ISKV_STATIC_SCRATCH_BYTES (16u << 20)
 
-typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1 } iskv_dtype;
+/* ISKV_I8 (coordinates only): low-bit history storage, the direction the
+ * page's section "Conclusion" names (integration with quantization) with no
+ * format given. The history keeps U = C Sigma^-1, the factor the equation for
+ * U+ rotates, as int8 codes with one fp32 scale per row: for a row u,
+ * scale = max|u| / 127 and code = round-half-even(127 u / max|u|) (a zero row
+ * has scale 0); history row i is reconstructed as (code_i * scale_i) Sigma B^T.
+ * Every fold stores the rotated old rows and the new rows again. Requires
+ * kv_dtype ISKV_BF16, ranks that are multiples of 8, (ncap + 65536) * r < 2^31
+ * and the joint update mode. */
+typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1, ISKV_I8 = 2 } iskv_dtype;
 
 /* Numeric status flags (bit mask returned by iskv_status). */
 #define ISKV_FLAG_SWEEP_CAP 0x1u /* a core SVD stopped at its sweep cap */
@@ -90,7 +99,7 @@ typedef struct {
   int32_t rank_v;      /* r_V, rank budget of values; 1 <= r_V <= 128 */
   int32_t window;      /* w >= 0: exact rows kept after a fold; w + 2b <= 4096 */
   int32_t max_tokens;  /* per-sequence capacity: n + e <= max_tokens */
-  int32_t coord_dtype; /* iskv_dtype of C = U Sigma; B and sigma are always fp32 */
+  int32_t coord_dtype; /* iskv_dtype of C = U Sigma (ISKV_I8: of U, see above); B and sigma are always fp32 */
   int32_t kv_dtype;    /* iskv_dtype of incoming rows, window, queries and outputs */
 } iskv_config;
 
@@ -109,7 +118,8 @@ ISKV_API int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, vo
 ISKV_API int iskv_reset(iskv_t h, void *stream);
 
 /* Select the update mode used by later folds of every layer (one of the
- * ISKV_MODE_* values; ISKV_ERR_ARG otherwise). Host state only; takes effect
+ * ISKV_MODE_* values; ISKV_ERR_ARG otherwise, and for any mode other than
+ * ISKV_MODE_JOINT with ISKV_I8 coordinates). Host state only; takes effect
  * with the next fold. */
 ISKV_API int iskv_set_mode(iskv_t h, int32_t mode);
 
@@ -208,7 +218,8 @@ ISKV_API int iskv_reconstruct(iskv_t h, int32_t which, int32_t batch, int32_t la
 ISKV_API int iskv_counts(iskv_t h, int32_t layer, int32_t *n, int32_t *e, int32_t *k_k, int32_t *k_v);
 
 /* Copy one unit's state out (device to device): C [n x r] in coord_dtype
- * (columns >= k are zero), sigma [r] fp32, Bt [r x d] fp32 (row j = basis
+ * (columns >= k are zero; with ISKV_I8 the int8 codes of U, whose per-row
+ * scales iskv_export_scales copies), sigma [r] fp32, Bt [r x d] fp32 (row j = basis
  * vector j), window [e x d] in kv_dtype oldest first. Any pointer may be NULL
  * to skip that part. */
 ISKV_API int iskv_export_state(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head, void *C,
@@ -229,6 +240,19 @@ ISKV_API int iskv_set_counts(iskv_t h, int32_t layer, int32_t n, int32_t e, int3
 ISKV_API int iskv_import_state(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head,
                       const void *C, const float *sigma, const float *Bt, const void *window,
                       void *stream);
+
+/* ISKV_I8 coordinates only (else ISKV_ERR_ARG): copy one unit's per-row
+ * scales of U out, scales [n] fp32 device memory, n = the layer's history rows
+ * (see ISKV_I8 for their meaning). Section "Reconstruction and Storage" (the
+ * stored history) with the int8 reading above. */
+ISKV_API int iskv_export_scales(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head,
+                                float *scales, void *stream);
+
+/* ISKV_I8 coordinates only: copy one unit's per-row scales in (device to
+ * device), layout as iskv_export_scales, with the layer's current counters;
+ * to be used with iskv_import_state. */
+ISKV_API int iskv_import_scales(iskv_t h, int32_t which, int32_t batch, int32_t layer, int32_t head,
+                                const float *scales, void *stream);
 
 /* Per-unit statistics of each unit's most recent fold (device to device):
  * sweeps [units] int32 = core SVD sweeps; discarded [units] fp32 = energy

@@ -78,8 +78,17 @@ bool valid_config(const iskv_config *c) {
   if (c->block < 1 || c->block > D) return false;
   if (c->rank_k < 1 || c->rank_k > D || c->rank_v < 1 || c->rank_v > D) return false;
   if (c->window < 0 || c->max_tokens < 1) return false;
-  if (c->coord_dtype != ISKV_F32 && c->coord_dtype != ISKV_BF16) return false;
+  if (c->coord_dtype != ISKV_F32 && c->coord_dtype != ISKV_BF16 && c->coord_dtype != ISKV_I8) return false;
   if (c->kv_dtype != ISKV_F32 && c->kv_dtype != ISKV_BF16) return false;
+  if (c->coord_dtype == ISKV_I8) {
+    // int8 rows run on the bf16 matrix-core kernels only: bf16 rows, ranks in
+    // whole 8-column pieces, and every byte offset of a unit's rows (plus one
+    // prefetch of rows) below 2^31
+    if (c->kv_dtype != ISKV_BF16 || c->rank_k % 8 != 0 || c->rank_v % 8 != 0) return false;
+    const long long ncap = (long long)(c->max_tokens / c->block) * c->block;
+    const int rm = c->rank_k > c->rank_v ? c->rank_k : c->rank_v;
+    if ((ncap + 65536) * rm >= (1LL << 31)) return false;
+  }
   const long long units = (long long)c->batch * c->layers * c->kv_heads;
   if (units > (1LL << 26)) return false;
   if ((long long)c->batch * c->kv_heads > MAX_UNITS_PER_LAUNCH) return false;
@@ -101,13 +110,14 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
   l.ncap = (c->max_tokens / c->block) * c->block;
   l.rcap = c->window + 2 * c->block;
   l.coord_bf16 = c->coord_dtype == ISKV_BF16;
+  l.coord_i8 = c->coord_dtype == ISKV_I8;
   l.kv_bf16 = c->kv_dtype == ISKV_BF16;
   l.units = c->batch * c->layers * c->kv_heads;
   l.chunk = 512 > l.rcap ? 512 : l.rcap;
   l.nchunk_max = (l.ncap + 511) / 512;  // every decode path uses >= 512 history rows per block
   if (l.nchunk_max < 1) l.nchunk_max = 1;
   const size_t U = (size_t)l.units;
-  const size_t cb = l.coord_bf16 ? 2 : 4, kb = l.kv_bf16 ? 2 : 4;
+  const size_t cb = l.coord_i8 ? 1 : l.coord_bf16 ? 2 : 4, kb = l.kv_bf16 ? 2 : 4;
   const int pmax = scratch_rows(c->block, c->rank_k, c->rank_v);
   size_t off = 0;
   auto take = [&](size_t bytes) -> void * {
@@ -119,8 +129,10 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
     const int r = x == 0 ? c->rank_k : c->rank_v;
     Stream &s = l.X[x];
     s.r = r;
-    s.cstride = (size_t)l.ncap * r + 256 / cb;
+    // int8 rows are read in 16-byte pieces: keep every unit's rows 16-byte aligned
+    s.cstride = l.coord_i8 ? ((size_t)l.ncap * r + 15) / 16 * 16 + 256 : (size_t)l.ncap * r + 256 / cb;
     s.C = take(U * s.cstride * cb);
+    s.cs = l.coord_i8 ? (float *)take(U * l.ncap * 4) : nullptr;
     s.Bt = (float *)take(U * r * D * 4);
     s.sig = (float *)take(U * r * 4);
     s.ring = take(U * l.rcap * D * kb);
@@ -227,7 +239,7 @@ int fold_run(iskv_t h, int l0, int l1, hipStream_t s) {
     ra.u0 = u0;
     ra.n = n;
     ra.ncap = L.ncap;
-    rc = fail_hip(h, launch_rewrite(ra, nunits, L.coord_bf16, s));
+    rc = fail_hip(h, L.coord_i8 ? launch_rewrite_i8(ra, nunits, s) : launch_rewrite(ra, nunits, L.coord_bf16, s));
     if (rc) return rc;
   }
   if (h->fev_on && fail_hip(h, hipEventRecord(h->fev[3], s))) return ISKV_ERR_HIP;
@@ -332,6 +344,7 @@ int iskv_set_mode(iskv_t h, int32_t mode) {
   if (!h) return ISKV_ERR_ARG;
   if (mode != ISKV_MODE_JOINT && mode != ISKV_MODE_FIXED_COORDS && mode != ISKV_MODE_FIXED_BASIS)
     return ISKV_ERR_ARG;
+  if (h->L.coord_i8 && mode != ISKV_MODE_JOINT) return ISKV_ERR_ARG;  // int8 storage: joint update only
   h->mode = mode;
   return ISKV_OK;
 }
@@ -412,6 +425,7 @@ int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32
     a.nl = l1 - l0;
     a.u0 = l0 * per_layer;
     a.nrows = nrows;
+    a.ncap = L.ncap;
     a.status = L.status;
     int rc = fail_hip(h, launch_oneshot(a, (l1 - l0) * per_layer, L.kv_bf16, L.coord_bf16, s));
     if (rc) return rc;
@@ -595,7 +609,7 @@ int iskv_export_state(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t
   const Stream &X = L.X[which];
   const int u = unit_index(h, b, layer, head);
   hipStream_t s = (hipStream_t)stream;
-  const size_t cb = L.coord_bf16 ? 2 : 4;
+  const size_t cb = L.coord_i8 ? 1 : L.coord_bf16 ? 2 : 4;
   if (C && h->n[layer] > 0) {
     const char *src = (const char *)X.C + (size_t)u * X.cstride * cb;
     if (fail_hip(h, hipMemcpyAsync(C, src, (size_t)h->n[layer] * X.r * cb, hipMemcpyDeviceToDevice, s)))
@@ -638,7 +652,7 @@ int iskv_import_state(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t
   const Stream &X = L.X[which];
   const int u = unit_index(h, b, layer, head);
   hipStream_t s = (hipStream_t)stream;
-  const size_t cb = L.coord_bf16 ? 2 : 4;
+  const size_t cb = L.coord_i8 ? 1 : L.coord_bf16 ? 2 : 4;
   if (C && h->n[layer] > 0) {
     char *dst = (char *)X.C + (size_t)u * X.cstride * cb;
     if (fail_hip(h, hipMemcpyAsync(dst, C, (size_t)h->n[layer] * X.r * cb, hipMemcpyDeviceToDevice, s)))
@@ -653,6 +667,31 @@ int iskv_import_state(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t
   if (window && fail_hip(h, launch_ring_copy(L, which, u, h->e[layer], h->head[layer], nullptr, window, 1, s)))
     return ISKV_ERR_HIP;
   return ISKV_OK;
+}
+
+static int copy_scales(iskv_t h, int which, int b, int layer, int head, float *out, const float *in,
+                       void *stream) {
+  if (!h || (!out && !in)) return ISKV_ERR_ARG;
+  if (h->poisoned) return ISKV_ERR_POISONED;
+  if (bad_unit(h, which, b, layer, head) || !h->L.coord_i8) return ISKV_ERR_ARG;
+  const Stream &X = h->L.X[which];
+  float *sc = X.cs + (size_t)unit_index(h, b, layer, head) * h->L.ncap;
+  const size_t bytes = (size_t)h->n[layer] * 4;
+  if (bytes == 0) return ISKV_OK;
+  return fail_hip(h, out ? hipMemcpyAsync(out, sc, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream)
+                         : hipMemcpyAsync(sc, in, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+}
+
+int iskv_export_scales(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t head, float *scales,
+                       void *stream) {
+  if (!scales) return ISKV_ERR_ARG;
+  return copy_scales(h, which, b, layer, head, scales, nullptr, stream);
+}
+
+int iskv_import_scales(iskv_t h, int32_t which, int32_t b, int32_t layer, int32_t head, const float *scales,
+                       void *stream) {
+  if (!scales) return ISKV_ERR_ARG;
+  return copy_scales(h, which, b, layer, head, nullptr, scales, stream);
 }
 
 int iskv_fold_stats(iskv_t h, int32_t which, int32_t *sweeps, float *discarded, void *stream) {

@@ -31,7 +31,9 @@ inline int scratch_rows(int block, int rank_k, int rank_v) {
 }
 
 struct Stream {
-  void *C;          // [U][cstride] coordinates C = U Sigma (coord dtype): ncap rows of r, zero beyond column k
+  void *C;          // [U][cstride] coordinates C = U Sigma (coord dtype): ncap rows of r, zero beyond column k;
+                    // int8 storage keeps U = C Sigma^-1 here as codes, one scale per row in cs
+  float *cs;        // [U][ncap] int8 storage: scale of each stored row of U (nullptr otherwise)
   float *Bt;        // [U][r][D] basis vectors as rows, zero beyond row k
   float *sig;       // [U][r] singular values, zero beyond k
   void *ring;       // [U][rcap][D] exact window ring (kv dtype)
@@ -49,6 +51,7 @@ struct Layout {
   int batch, layers, kvh, qh, g;  // g = query heads per kv head
   int b, w, ncap, rcap;           // block, window, history capacity, ring capacity
   int coord_bf16, kv_bf16;
+  int coord_i8;                   // int8 codes of U with per-row scales (coord_bf16 is 0 then)
   int units;                      // batch * layers * kvh
   Stream X[2];                    // 0 = K, 1 = V
   uint32_t *status;               // [16] sticky numeric flags
@@ -116,6 +119,7 @@ struct OneshotArgs {
   const void *src[2];  // K, V rows [batch][nl_in][kvh][nrows][D]
   int batch, kvh, nl_in, lrel0, nl;
   int u0, nrows;
+  int ncap;  // history capacity (rows per unit of the int8 scale arrays)
   uint32_t *status;
 };
 
@@ -161,6 +165,29 @@ __device__ __forceinline__ float sum64(float v) {
   return sum16(v);
 }
 
+// int8 storage of a row of U: scale = max|u| / 127, code = round-half-even(u * 127 / max|u|),
+// the rounding decision taken in fp32 from the row's own maximum
+__device__ __forceinline__ float i8_inv_step(float m) { return m > 0.f ? 127.f / m : 0.f; }
+__device__ __forceinline__ int i8_code(float v, float inv) {
+  const float q = rintf(v * inv);
+  return (int)fminf(fmaxf(q, -127.f), 127.f);
+}
+
+// bf16 bits of a small integer (exact: |x| <= 256)
+__device__ __forceinline__ uint32_t int_bf16(int x) { return __float_as_uint((float)x) >> 16; }
+
+// eight int8 codes (two dwords, low byte first) as eight bf16 values packed in
+// four dwords, the operand layout of the bf16 matrix-core instructions
+__device__ __forceinline__ void i8x8_bf16(uint32_t w0, uint32_t w1, uint32_t out[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const uint32_t w = e < 2 ? w0 : w1;
+    const int sh = 16 * (e & 1);
+    const int lo = ((int)(w << (24 - sh))) >> 24, hi = ((int)(w << (16 - sh))) >> 24;
+    out[e] = int_bf16(lo) | (int_bf16(hi) << 16);
+  }
+}
+
 __device__ __forceinline__ float max64(float v) {
   v = fmaxf(v, __shfl_xor(v, 32));
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -180,6 +207,8 @@ hipError_t launch_core(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf1
 size_t fold_core_lds_bytes(int k, int b, int r);
 hipError_t launch_fold(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
 hipError_t launch_rewrite(const RewriteArgs &a, int nunits, int coord_bf16, hipStream_t s);  // K and V
+// int8 storage: U <- U M in place with per-row scales, M = Sigma_old H_top Sigma_new^-1 (in Htop)
+hipError_t launch_rewrite_i8(const RewriteArgs &a, int nunits, hipStream_t s);
 hipError_t launch_ingest(const IngestArgs &a, int kv_bf16, hipStream_t s);
 // fixed-basis fold: new rows C[n + i] = F_i B (k columns), discarded energy
 hipError_t launch_project(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s);
@@ -190,6 +219,8 @@ hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coo
 // coordinates, ranks multiples of 8
 bool oneshot_coords_mfma_ok(const OneshotArgs &a, int kv_bf16, int coord_bf16);
 hipError_t launch_oneshot_coords_mfma(const OneshotArgs &a, int nunits, hipStream_t s);
+// int8 storage: sigma = column norms of X B^T, then U = X B^T Sigma^-1 stored per row
+hipError_t launch_oneshot_coords_i8(const OneshotArgs &a, int nunits, hipStream_t s);
 // true when launch_decode can take the appended row itself (nnew = 1)
 bool decode_can_fuse(const DecodeArgs &a);
 // true when the split (matrix-core) decode applies to these counters

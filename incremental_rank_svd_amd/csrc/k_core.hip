@@ -1221,6 +1221,7 @@ hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coo
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.X[0].cs) return launch_oneshot_coords_i8(a, nunits, s);  // int8 storage of U (bf16 rows)
   if (oneshot_coords_mfma_ok(a, kv_bf16, coord_bf16)) return launch_oneshot_coords_mfma(a, nunits, s);
   const int rmin = a.X[0].r < a.X[1].r ? a.X[0].r : a.X[1].r;
   const int rmax = a.X[0].r > a.X[1].r ? a.X[0].r : a.X[1].r;

@@ -403,6 +403,68 @@ __device__ __forceinline__ void store_tile(uint16_t *tile, int ts, int rsV, int 
   }
 }
 
+// int8 storage: the same step over codes of U. Lane l takes the 8 codes of
+// columns 32 kc + 8 (l / 16) .. +7 of rows rb + l % 16 and rb + 16 + l % 16
+// (8 bytes each), the 32-row C_V tile is 32 rsV contiguous bytes read in
+// 16-byte pieces, and each lane takes the scales of the 8 rows its score
+// fragments hold (rows rb + 4 (l / 16) + i and rb + 16 + 4 (l / 16) + i);
+// rows at or past `we` get scale 0.
+template <int KS, int NV>
+__device__ __forceinline__ void load_step_i8(const uint8_t *CK, const uint8_t *CV, const float *sK,
+                                             const float *sV, int rsK, int rsV, int rb, int we, int lane,
+                                             uint2 *ka, uint2 *kb, u32x4_t *vv, float *fk, float *fv) {
+  const int hq = lane & 15, qd = lane >> 4;
+#pragma unroll
+  for (int kc = 0; kc < KS; kc++) {
+    const int col = kc * 32 + 8 * qd;
+    const int r0 = rb + hq, r1 = rb + 16 + hq;
+    ka[kc] = uint2{0u, 0u};
+    kb[kc] = uint2{0u, 0u};
+    if (col < rsK) {
+      if (r0 < we) ka[kc] = *(const uint2 *)(CK + (size_t)r0 * rsK + col);
+      if (r1 < we) kb[kc] = *(const uint2 *)(CK + (size_t)r1 * rsK + col);
+    }
+  }
+#pragma unroll
+  for (int z = 0; z < NV; z++) {
+    const int idx = lane + 64 * z;
+    vv[z] = u32x4_t{0u, 0u, 0u, 0u};
+    // a piece's first byte decides the load; its second half may reach row
+    // we, which is still inside the unit's rows or its 256-byte pad
+    if (idx < 2 * rsV && rb + (16 * idx) / rsV < we)
+      vv[z] = *(const u32x4_t *)(CV + (size_t)rb * rsV + 16 * idx);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int row = rb + ((i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4));
+    fk[i] = row < we ? sK[row] : 0.f;
+    fv[i] = row < we ? sV[row] : 0.f;
+  }
+}
+
+// the 16-byte pieces of the C_V tile as bf16 into the wave's LDS tile; each
+// 8-code half goes to its own row (rows past we as zeros)
+template <int NV>
+__device__ __forceinline__ void store_tile_i8(uint16_t *tile, int ts, int rsV, int rb, int we, int lane,
+                                              const u32x4_t *vv) {
+#pragma unroll
+  for (int z = 0; z < NV; z++) {
+    const int idx = lane + 64 * z;
+    if (idx < 2 * rsV) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int off = 16 * idx + 8 * h;
+        const int rr = off / rsV, c = off - rr * rsV;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (rb + rr < we) i8x8_bf16(vv[z][2 * h], vv[z][2 * h + 1], w);
+        uint2 *dstp = (uint2 *)(tile + rr * ts + c);
+        dstp[0] = uint2{w[0], w[1]};
+        dstp[1] = uint2{w[2], w[3]};
+      }
+    }
+  }
+}
+
 // Window rows of one unit straight from the ring (used when the window does
 // not fit in LDS): row i goes to lane group (i mod 64) of the workgroup (16
 // lanes per 128-wide row), WH heads per pass, online softmax; the 4 lane
@@ -569,7 +631,10 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u3
 // [s split_rows, (s + 1) split_rows) and workgroup 0 also the window; each
 // leaves its partial (max, sum, o', window values) per query head in
 // a.spart for k_decode_merge instead of writing the output.
-template <int KS, int NTV, bool SPLIT>
+// I8: int8 storage of U with per-row scales (scores C_K q' = U_K (Sigma_K q'),
+// values p^T C_V = (p^T U_V) Sigma_V, each row's scale on its score and its
+// softmax weight).
+template <int KS, int NTV, bool SPLIT, bool I8>
 __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   extern __shared__ float sm[];
   const int ul = blockIdx.x, u = a.u0 + ul;
@@ -635,10 +700,24 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   const int we = min(h1, wb + per);
   const uint16_t *CK = (const uint16_t *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride;
   const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
+  const uint8_t *CK8 = (const uint8_t *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride;
+  const uint8_t *CV8 = (const uint8_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
+  const float *sK = I8 ? a.L.X[0].cs + (size_t)u * a.L.ncap : nullptr;
+  const float *sV = I8 ? a.L.X[1].cs + (size_t)u * a.L.ncap : nullptr;
   // prefetching the next step doubles the load registers: only when they fit
-  constexpr bool PF = (NTV + 2 * KS) <= 6;
-  u32x4_t ka[KS], kb[KS], vv[NTV];
-  if (PF && wb < we) load_step<KS, NTV>(CK, CV, rsK, rsV, wb, we, lane, ka, kb, vv);
+  constexpr int NV = I8 ? (NTV + 1) / 2 : NTV;  // 16-byte pieces of the C_V tile per lane
+  constexpr bool PF = I8 ? (NV + KS) <= 2 : (NTV + 2 * KS) <= 6;  // int8: 8 row scales per kind too
+  u32x4_t ka[KS], kb[KS], vv[NV];
+  uint2 ka8[KS], kb8[KS];
+  float fk[8], fv[8];
+  auto load = [&](int rb, u32x4_t *ka_, u32x4_t *kb_, uint2 *ka8_, uint2 *kb8_, u32x4_t *vv_, float *fk_,
+                  float *fv_) {
+    if constexpr (I8)
+      load_step_i8<KS, NV>(CK8, CV8, sK, sV, rsK, rsV, rb, we, lane, ka8_, kb8_, vv_, fk_, fv_);
+    else
+      load_step<KS, NTV>(CK, CV, rsK, rsV, rb, we, lane, ka_, kb_, vv_);
+  };
+  if (PF && wb < we) load(wb, ka, kb, ka8, kb8, vv, fk, fv);
   // q' = scale * B_K^T q, zero beyond the current rank (16 lanes per dot)
   {
     const float *Bt = a.L.X[0].Bt + (size_t)u * rsK * D;
@@ -651,6 +730,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
         for (int t = 0; t < 8; t++) s += Bt[(size_t)jj * D + l16 * 8 + t] * bf2f(q[(size_t)hh * D + l16 * 8 + t]);
       }
       s = sum16(s);
+      if constexpr (I8) s *= (jj < a.kK) ? a.L.X[0].sig[(size_t)u * rsK + jj] : 0.f;  // Sigma_K q'
       if (l16 == 0) qsm[hh * rsK + jj] = a.scale * s;
     }
   }
@@ -691,20 +771,38 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   {
     const int ts = tile_stride(rsV);
     uint16_t *tile = (uint16_t *)big + (size_t)wv * 32 * ts;
+    auto put_tile = [&](int rb, const u32x4_t *vv_) {
+      if constexpr (I8)
+        store_tile_i8<NV>(tile, ts, rsV, rb, we, lane, vv_);
+      else
+        store_tile<NTV>(tile, ts, rsV, lane, vv_);
+    };
     if (wb < we) {
       if constexpr (PF) {
-        store_tile<NTV>(tile, ts, rsV, lane, vv);
+        put_tile(wb, vv);
         wave_fence();
       }
       for (int rb = wb; rb < we; rb += 32) {
         const bool more = rb + 32 < we;
-        u32x4_t nka[KS], nkb[KS], nvv[NTV];
+        u32x4_t nka[KS], nkb[KS], nvv[NV];
+        uint2 nka8[KS], nkb8[KS];
+        float nfk[8], nfv[8];
         if constexpr (PF) {
-          if (more) load_step<KS, NTV>(CK, CV, rsK, rsV, rb + 32, we, lane, nka, nkb, nvv);
+          if (more) load(rb + 32, nka, nkb, nka8, nkb8, nvv, nfk, nfv);
         } else {
-          load_step<KS, NTV>(CK, CV, rsK, rsV, rb, we, lane, ka, kb, vv);
-          store_tile<NTV>(tile, ts, rsV, lane, vv);
+          load(rb, ka, kb, ka8, kb8, vv, fk, fv);
+          put_tile(rb, vv);
           wave_fence();
+        }
+        if constexpr (I8) {
+#pragma unroll
+          for (int kc = 0; kc < KS; kc++) {
+            uint32_t w[4];
+            i8x8_bf16(ka8[kc].x, ka8[kc].y, w);
+            ka[kc] = u32x4_t{w[0], w[1], w[2], w[3]};
+            i8x8_bf16(kb8[kc].x, kb8[kc].y, w);
+            kb[kc] = u32x4_t{w[0], w[1], w[2], w[3]};
+          }
         }
         f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -718,8 +816,10 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
         float s[8];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          s[i] = (rb + 4 * qd + i < we) ? d0[i] : -INFINITY;
-          s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] : -INFINITY;
+          // int8 storage: each row's score takes its scale
+          const float f0 = I8 ? fk[i] : 1.f, f1 = I8 ? fk[4 + i] : 1.f;
+          s[i] = (rb + 4 * qd + i < we) ? d0[i] * f0 : -INFINITY;
+          s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] * f1 : -INFINITY;
         }
         float mx = s[0];
 #pragma unroll
@@ -740,7 +840,14 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NTV; nt++) acc[nt] *= al;
         u32x4_t phi, plo;
-        split8(p, phi, plo);
+        if constexpr (I8) {
+          float pv[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) pv[i] = p[i] * fv[i];
+          split8(pv, phi, plo);
+        } else {
+          split8(p, phi, plo);
+        }
 #pragma unroll
         for (int nt = 0; nt < NTV; nt++) {
           const int col = nt * 16 + hq;
@@ -757,11 +864,18 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
         wave_fence();
         if constexpr (PF) {
           if (more) {
-            store_tile<NTV>(tile, ts, rsV, lane, nvv);
+            put_tile(rb + 32, nvv);
 #pragma unroll
             for (int kc = 0; kc < KS; kc++) {
               ka[kc] = nka[kc];
               kb[kc] = nkb[kc];
+              ka8[kc] = nka8[kc];
+              kb8[kc] = nkb8[kc];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              fk[i] = nfk[i];
+              fv[i] = nfv[i];
             }
           }
           wave_fence();
@@ -799,12 +913,14 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       hm[wv * MAXG + hq] = m;
       hl[wv * MAXG + hq] = l;
     }
+    const float *sgV = a.L.X[1].sig + (size_t)u * rsV;
 #pragma unroll
     for (int nt = 0; nt < NTV; nt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int col = nt * 16 + 4 * qd + i;
-        if (col < rsV) ha[((size_t)wv * g + hq) * rsV + col] = acc[nt][i];
+        // int8 storage holds U_V: o' = (p^T U_V) Sigma_V
+        if (col < rsV) ha[((size_t)wv * g + hq) * rsV + col] = I8 ? acc[nt][i] * sgV[col] : acc[nt][i];
       }
   }
   // ---- window rows: row i goes to lane group (i mod 64) of the workgroup ----
@@ -944,7 +1060,7 @@ __global__ void __launch_bounds__(NT) k_decode_merge(const DecodeArgs a) {
   }
 }
 
-template <int KS, int NTV>
+template <int KS, int NTV, bool I8>
 hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
   DecodeArgs a = a0;
   // stage the window in LDS when it fits next to the rest (160 KB per workgroup)
@@ -953,33 +1069,43 @@ hipError_t launch_bf16_t(const DecodeArgs &a0, int nunits, hipStream_t s) {
   a.wlds = (ew > 0 && lds <= 160 * 1024 && ((uintptr_t)a.q & 15) == 0) ? 1 : 0;
   if (!a.wlds) lds = decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, 0);
   if (a.nsplit > 0) {
-    hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, true>,
+    hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, true, I8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_decode_unit<KS, NTV, true>), dim3(nunits, a.nsplit), dim3(NTU), lds, s, a);
+    hipLaunchKernelGGL((k_decode_unit<KS, NTV, true, I8>), dim3(nunits, a.nsplit), dim3(NTU), lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_decode_merge, dim3(nunits), dim3(NT), 0, s, a);
     return hipGetLastError();
   }
-  hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, false>,
+  hipError_t e = hipFuncSetAttribute((const void *)k_decode_unit<KS, NTV, false, I8>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_unit<KS, NTV, false>), dim3(nunits), dim3(NTU), lds, s, a);
+  hipLaunchKernelGGL((k_decode_unit<KS, NTV, false, I8>), dim3(nunits), dim3(NTU), lds, s, a);
   return hipGetLastError();
 }
 
-template <int KS>
+template <int KS, bool I8>
 hipError_t launch_bf16_ks(const DecodeArgs &a, int nunits, hipStream_t s) {
   switch ((a.L.X[1].r + 15) / 16) {
-    case 1: return launch_bf16_t<KS, 1>(a, nunits, s);
-    case 2: return launch_bf16_t<KS, 2>(a, nunits, s);
-    case 3: return launch_bf16_t<KS, 3>(a, nunits, s);
-    case 4: return launch_bf16_t<KS, 4>(a, nunits, s);
-    case 5: return launch_bf16_t<KS, 5>(a, nunits, s);
-    case 6: return launch_bf16_t<KS, 6>(a, nunits, s);
-    case 7: return launch_bf16_t<KS, 7>(a, nunits, s);
-    default: return launch_bf16_t<KS, 8>(a, nunits, s);
+    case 1: return launch_bf16_t<KS, 1, I8>(a, nunits, s);
+    case 2: return launch_bf16_t<KS, 2, I8>(a, nunits, s);
+    case 3: return launch_bf16_t<KS, 3, I8>(a, nunits, s);
+    case 4: return launch_bf16_t<KS, 4, I8>(a, nunits, s);
+    case 5: return launch_bf16_t<KS, 5, I8>(a, nunits, s);
+    case 6: return launch_bf16_t<KS, 6, I8>(a, nunits, s);
+    case 7: return launch_bf16_t<KS, 7, I8>(a, nunits, s);
+    default: return launch_bf16_t<KS, 8, I8>(a, nunits, s);
+  }
+}
+
+template <bool I8>
+hipError_t launch_unit_path(const DecodeArgs &a, int nunits, hipStream_t s) {
+  switch ((a.L.X[0].r + 31) / 32) {
+    case 1: return launch_bf16_ks<1, I8>(a, nunits, s);
+    case 2: return launch_bf16_ks<2, I8>(a, nunits, s);
+    case 3: return launch_bf16_ks<3, I8>(a, nunits, s);
+    default: return launch_bf16_ks<4, I8>(a, nunits, s);
   }
 }
 
@@ -997,27 +1123,25 @@ hipError_t launch_decode_t(const DecodeArgs &a, int nunits, hipStream_t s) {
 
 int decode_chunk_rows(const Layout &L) { return L.chunk; }
 
+// the matrix-core decode: bf16 or int8 coordinates, bf16 rows, ranks in 8-column pieces
+static bool unit_path(const Layout &L) {
+  return (L.coord_bf16 || L.coord_i8) && L.kv_bf16 && L.X[0].r % 8 == 0 && L.X[1].r % 8 == 0;
+}
+
 bool decode_can_fuse(const DecodeArgs &a) {
-  if (!(a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0)) return false;
+  if (!unit_path(a.L)) return false;
   if ((((uintptr_t)a.q | (uintptr_t)a.nk | (uintptr_t)a.nv) & 15) != 0) return false;
   return decode_unit_lds(a.L.X[0].r, a.L.X[1].r, a.L.g, a.e + 1) <= 160 * 1024;
 }
 
 bool decode_can_split(const DecodeArgs &a) {
-  if (!(a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0)) return false;
+  if (!unit_path(a.L)) return false;
   return a.nnew == 0;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   const int nunits = a.L.batch * a.nl * a.L.kvh;
-  if (a.L.coord_bf16 && a.L.kv_bf16 && a.L.X[0].r % 8 == 0 && a.L.X[1].r % 8 == 0) {
-    switch ((a.L.X[0].r + 31) / 32) {
-      case 1: return launch_bf16_ks<1>(a, nunits, s);
-      case 2: return launch_bf16_ks<2>(a, nunits, s);
-      case 3: return launch_bf16_ks<3>(a, nunits, s);
-      default: return launch_bf16_ks<4>(a, nunits, s);
-    }
-  }
+  if (unit_path(a.L)) return a.L.coord_i8 ? launch_unit_path<true>(a, nunits, s) : launch_unit_path<false>(a, nunits, s);
   if (a.L.coord_bf16 && a.L.kv_bf16) return launch_decode_t<uint16_t, uint16_t>(a, nunits, s);
   if (a.L.coord_bf16) return launch_decode_t<uint16_t, float>(a, nunits, s);
   if (a.L.kv_bf16) return launch_decode_t<float, uint16_t>(a, nunits, s);

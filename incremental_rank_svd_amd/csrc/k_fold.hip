@@ -25,6 +25,8 @@
 // Work mapping: quads (4 lanes) own one column in the two QRs and of P;
 // octets (8 lanes) own one Jacobi pair, 64 pairs per round, so a 128-column
 // core keeps all 8 waves busy with 16 rows per lane.
+#include <type_traits>
+
 #include "fold_common.hpp"
 
 namespace iskv {
@@ -775,7 +777,8 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
         if (i < c && jr < kplus) Hn[(size_t)jr * sj + i] = sgn[jr] * H[(size_t)perm[jr] * sj + i] + v;
       });
   __syncthreads();
-  {
+  constexpr bool I8 = std::is_same<TC, int8_t>::value;
+  if constexpr (!I8) {
     float *Ht = X.Htop + (size_t)u * r * r;
     for (int idx = tid; idx < k * kplus; idx += NTF) {
       const int i = idx / kplus, jr = idx - i * kplus;
@@ -800,7 +803,13 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
 #pragma unroll
           for (int v = 0; v < 4; v++) {
             const int i = i0 + 4 * lk + v;
-            if (i < b && jr < r) stf<TC>(Cn, (size_t)i * r + jr, acc[v]);
+            if constexpr (I8) {
+              // int8 storage needs the new sigma first: the rows wait in the
+              // fold scratch (free since H_r G)
+              if (i < b && jr < r) Pg[(size_t)i * r + jr] = acc[v];
+            } else {
+              if (i < b && jr < r) stf<TC>(Cn, (size_t)i * r + jr, acc[v]);
+            }
             sq += acc[v] * acc[v];  // zero for rows past b
           }
           sq += __shfl_xor(sq, 16);
@@ -813,6 +822,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
   // (orthogonal columns of norms sigma_old, so sum_l sigma_l^2 Hn[l][j]^2)
   // plus the new rows. Computing it from what is stored keeps the next
   // fold's Z an exact description of the stored history.
+  float *sgnew = smem;  // H's region, dead since H_r G: the new sigma for int8 storage
   if (tid < r) {
     float s2 = 0.f;
     if (tid < kplus) {
@@ -821,6 +831,43 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       for (int mt = 0; mt < (b + 15) / 16; mt++) s2 += sqp[mt * r + tid];
     }
     X.sig[(size_t)u * r + tid] = sqrtf(s2);
+    if constexpr (I8) {
+      if (tid < kplus) sgnew[tid] = sqrtf(s2);  // kplus <= c floats, below H_r G at c * sj
+    }
+  }
+  if constexpr (I8) {
+    // int8 storage keeps U = C Sigma^-1. The stored rows of U rotate by
+    // M = Sigma_old H_top Sigma_new^-1 (C_old H_top = U_old M Sigma_new); the
+    // new rows of U are the new rows of C over the new sigma, each stored as
+    // int8 codes with its own scale (max|u| / 127). A column with sigma 0 is
+    // zero in C, so its U column is written as zero.
+    __syncthreads();
+    float *Ht = X.Htop + (size_t)u * r * r;
+    for (int idx = tid; idx < k * kplus; idx += NTF) {
+      const int i = idx / kplus, jr = idx - i * kplus;
+      const float sn = sgnew[jr];
+      Ht[(size_t)i * r + jr] = sn > 0.f ? tau[i] * Hn[(size_t)jr * sj + i] / sn : 0.f;
+    }
+    int8_t *Cn = (int8_t *)X.C + (size_t)u * X.cstride + (size_t)a.n * r;
+    float *cs = X.cs + (size_t)u * a.ncap + a.n;
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int i = wv; i < b; i += NW) {
+      float v[2];
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int j = ln + 64 * h;
+        const float sn = j < kplus ? sgnew[j] : 0.f;
+        v[h] = sn > 0.f ? Pg[(size_t)i * r + j] / sn : 0.f;
+      }
+      const float m = max64(fmaxf(fabsf(v[0]), fabsf(v[1])));
+      const float inv = i8_inv_step(m);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int j = ln + 64 * h;
+        if (j < r) Cn[(size_t)i * r + j] = (int8_t)i8_code(v[h], inv);
+      }
+      if (ln == 0) cs[i] = m / 127.f;
+    }
   }
 }
 
@@ -859,6 +906,7 @@ hipError_t launch_fold_nr(const FoldArgs &a, int nunits, hipStream_t s) {
 size_t fold_core_lds_bytes(int k, int b, int r) { return sizeof(float) * (size_t)fold_lds(k, b, r).total; }
 
 hipError_t launch_fold(const FoldArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
+  if (a.X[0].cs) return launch_fold_nr<uint16_t, int8_t>(a, nunits, s);  // int8 storage of U (bf16 rows)
   if (kv_bf16 && coord_bf16) return launch_fold_nr<uint16_t, uint16_t>(a, nunits, s);
   if (kv_bf16 && !coord_bf16) return launch_fold_nr<uint16_t, float>(a, nunits, s);
   if (!kv_bf16 && coord_bf16) return launch_fold_nr<float, uint16_t>(a, nunits, s);

@@ -106,6 +106,25 @@ __global__ void __launch_bounds__(NT) k_reconstruct(const float *Bt, const TC *C
   }
 }
 
+// int8 storage: history row = (codes * scale) Sigma B^T
+__global__ void __launch_bounds__(NT) k_reconstruct_i8(const float *Bt, const int8_t *C, const float *cs,
+                                                       const float *sig, const uint16_t *ring, int r, int n,
+                                                       int k, int e, int head, int rcap, float *out) {
+  const int row = blockIdx.x;
+  if (row < n) {
+    const float sc = cs[row];
+    for (int t = threadIdx.x; t < D; t += NT) {
+      float s = 0.f;
+      for (int j = 0; j < k; j++) s += ((float)C[(size_t)row * r + j] * sc) * sig[j] * Bt[(size_t)j * D + t];
+      out[(size_t)row * D + t] = s;
+    }
+  } else {
+    int pos = head + (row - n);
+    if (pos >= rcap) pos -= rcap;
+    for (int t = threadIdx.x; t < D; t += NT) out[(size_t)row * D + t] = bf2f(ring[(size_t)pos * D + t]);
+  }
+}
+
 __global__ void k_zero(uint32_t *p, size_t nwords) {
   for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < nwords; i += (size_t)gridDim.x * NT) p[i] = 0u;
 }
@@ -167,6 +186,12 @@ hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, i
   const float *Bt = X.Bt + (size_t)u * X.r * D;
   const size_t coff = (size_t)u * X.cstride;
   const size_t roff = (size_t)u * L.rcap * D;
+  if (L.coord_i8) {
+    hipLaunchKernelGGL(k_reconstruct_i8, dim3(rows), dim3(NT), 0, s, Bt, (const int8_t *)X.C + coff,
+                       X.cs + (size_t)u * L.ncap, X.sig + (size_t)u * X.r, (const uint16_t *)X.ring + roff, X.r,
+                       n, k, e, head, L.rcap, out);
+    return hipGetLastError();
+  }
   if (L.coord_bf16 && L.kv_bf16)
     hipLaunchKernelGGL((k_reconstruct<uint16_t, uint16_t>), dim3(rows), dim3(NT), 0, s, Bt,
                        (const uint16_t *)X.C + coff, (const uint16_t *)X.ring + roff, X.r, n, k, e, head,

@@ -28,6 +28,7 @@ ISKV_ERR_SCRATCH = -8
 
 ISKV_F32 = 0
 ISKV_BF16 = 1
+ISKV_I8 = 2  # coordinates only: int8 codes of U with one fp32 scale per row
 MODE_JOINT, MODE_FIXED_COORDS, MODE_FIXED_BASIS = 0, 1, 2  # ISKV_MODE_* in iskv.h
 FLAG_SWEEP_CAP = 0x1
 FLAG_NONFINITE = 0x2
@@ -37,7 +38,7 @@ EXPORTED = [
     "iskv_prefill_oneshot",
     "iskv_decode_attn", "iskv_append_decode", "iskv_reconstruct", "iskv_counts", "iskv_export_state", "iskv_set_counts",
     "iskv_import_state", "iskv_fold_stats", "iskv_status", "iskv_destroy", "iskv_strerror",
-    "iskv_set_fold_events", "iskv_decode_attn_static",
+    "iskv_set_fold_events", "iskv_decode_attn_static", "iskv_export_scales", "iskv_import_scales",
 ]
 
 
@@ -85,6 +86,8 @@ def load(path: str = None):
     lib.iskv_set_counts.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32]
     lib.iskv_import_state.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.iskv_fold_stats.argtypes = [_vp, _i32, _vp, _vp, _vp]
+    lib.iskv_export_scales.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
+    lib.iskv_import_scales.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
     lib.iskv_status.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.iskv_destroy.argtypes = [_vp]
     lib.iskv_strerror.argtypes = [ctypes.c_int]
@@ -111,7 +114,7 @@ def _check(code, what):
 
 def make_config(batch, layers, kv_heads, q_heads, block, rank_k, rank_v, window, max_tokens,
                 coord_dtype="bf16", kv_dtype="bf16", head_dim=128) -> Config:
-    dt = {"f32": ISKV_F32, "bf16": ISKV_BF16}
+    dt = {"f32": ISKV_F32, "bf16": ISKV_BF16, "i8": ISKV_I8}
     return Config(batch, layers, kv_heads, q_heads, head_dim, block, rank_k, rank_v, window,
                   max_tokens, dt[coord_dtype], dt[kv_dtype])
 
@@ -134,7 +137,7 @@ def _stream(stream):
     return _vp(stream)
 
 
-_TDT = {ISKV_F32: torch.float32, ISKV_BF16: torch.bfloat16}
+_TDT = {ISKV_F32: torch.float32, ISKV_BF16: torch.bfloat16, ISKV_I8: torch.int8}
 
 
 class Cache:
@@ -279,6 +282,21 @@ class Cache:
                                           _vp(sig.data_ptr()), _vp(Bt.data_ptr()), _vp(W.data_ptr()),
                                           _stream(stream)), "iskv_export_state")
         return C, sig, Bt, W
+
+    def export_scales(self, which, batch, layer, head, stream=None):
+        """int8 coordinates only: the per-row scales of U [n] fp32 (history row i is
+        (C[i] * scale[i]) * sigma B^T)."""
+        n, _, _, _ = self.counts(layer)
+        sc = torch.empty(n, dtype=torch.float32, device=self.device)
+        _check(self.lib.iskv_export_scales(self.h, which, batch, layer, head, _vp(sc.data_ptr()),
+                                           _stream(stream)), "iskv_export_scales")
+        return sc
+
+    def import_scales(self, which, batch, layer, head, scales, stream=None):
+        n, _, _, _ = self.counts(layer)
+        sp = self._t(scales, (n,), torch.float32, "scales")
+        _check(self.lib.iskv_import_scales(self.h, which, batch, layer, head, sp, _stream(stream)),
+               "iskv_import_scales")
 
     def set_counts(self, layer, n, e, k_k, k_v):
         _check(self.lib.iskv_set_counts(self.h, layer, n, e, k_k, k_v), "iskv_set_counts")

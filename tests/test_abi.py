@@ -70,7 +70,11 @@ def _cfg(**kw):
 @pytest.mark.parametrize("bad", [dict(head_dim=64), dict(q_heads=7), dict(block=0), dict(block=129),
                                  dict(rank_k=0), dict(rank_v=129), dict(window=-1),
                                  dict(max_tokens=0), dict(q_heads=2 * 9), dict(batch=0),
-                                 dict(coord_dtype="f32", kv_dtype="f32", layers=0)])
+                                 dict(coord_dtype="f32", kv_dtype="f32", layers=0),
+                                 # int8 coordinates: bf16 rows, ranks in 8-column pieces, offsets < 2^31
+                                 dict(coord_dtype="i8", kv_dtype="f32"), dict(coord_dtype="i8", rank_k=28),
+                                 dict(coord_dtype="i8", rank_v=100),
+                                 dict(coord_dtype="i8", rank_k=128, max_tokens=1 << 24)])
 def test_invalid_configs_rejected_on_host(lib, bad):
     from incremental_rank_svd_amd import iskv
 
@@ -79,6 +83,17 @@ def test_invalid_configs_rejected_on_host(lib, bad):
     h = ctypes.c_void_p()
     rc = lib.iskv_init(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), 1 << 40, None, ctypes.byref(h))
     assert rc == iskv.ISKV_ERR_ARG and not h.value
+
+
+def test_int8_coordinates_take_a_byte_per_entry_and_a_row_scale(lib):
+    # per unit and kind: ncap r codes (16-byte rounded, 256-byte pad) and ncap fp32 scales
+    # instead of 2 ncap r bytes of bf16
+    base = dict(batch=2, layers=4, kv_heads=8, q_heads=32, rank_k=64, rank_v=96, max_tokens=16384)
+    bf = lib.iskv_workspace_bytes(ctypes.byref(_cfg(**base)))
+    i8 = lib.iskv_workspace_bytes(ctypes.byref(_cfg(coord_dtype="i8", **base)))
+    U, ncap = 2 * 4 * 8, 16384
+    saved = U * ncap * (64 + 96) - 2 * U * ncap * 4
+    assert abs((bf - i8) - saved) <= 4 * U * 512, (bf, i8, saved)
 
 
 def test_workspace_checks_before_any_device_work(lib):
