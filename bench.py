@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--coords", choices=("f32", "bf16", "i8"), default=None,
                    help="stored coordinate type (default: the workload's); i8 = int8 codes of U with "
                         "one fp32 scale per row")
+    p.add_argument("--summarize-traffic", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                   help="write profiles/traffic_<workload>[_i8].json from four rocprofv3 --pmc output "
+                        "folders (copy calibration FETCH_SIZE, WRITE_SIZE; bench FETCH_SIZE, WRITE_SIZE)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device-to-device copy and exit (reference for HBM byte counters)")
     return p.parse_args()
@@ -559,6 +562,65 @@ def prefill_bench(args):
     }), flush=True)
 
 
+def _pmc_rows(folder):
+    """(kernel name, counter value) of every dispatch in a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+
+    out = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                out.append((row.get("Kernel_Name", ""), float(row.get("Counter_Value", 0.0))))
+    return out
+
+
+def summarize_traffic(args, w, scale_b):
+    """HBM bytes per launch of the fold core, the rewrite and the decode from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same
+    counter reads for the plain 1 GiB copy of --copy-calibration; the bench
+    run is --steps 1 --warmup 1 (two fold rounds, two decodes). Written with
+    each kernel's source hash: bench.py reports it only while that matches."""
+    cf, cw, fe, wr = args.summarize_traffic
+    gib_kib = float(1 << 20)
+    copy_f = max(v for k, v in _pmc_rows(cf) if "elementwise" in k or "mul" in k.lower())
+    copy_w = max(v for k, v in _pmc_rows(cw) if "elementwise" in k or "mul" in k.lower())
+    ff, wf = gib_kib / copy_f, gib_kib / copy_w
+    groups = {"k_fold": ("k_fold.hip", "iskv::k_fold<"),
+              ("k_rewrite_i8" if scale_b else "k_rewrite_mfma"):
+                  ("k_rewrite.hip", "iskv::k_rewrite_i8<" if scale_b else "iskv::k_rewrite_mfma<"),
+              "k_decode_unit": ("k_decode.hip", "iskv::k_decode_unit<")}
+    fetch, write = _pmc_rows(fe), _pmc_rows(wr)
+    kern = {}
+    for name, (src, prefix) in groups.items():
+        key = prefix.split("::")[-1]
+        fs = [v for k, v in fetch if key in k]
+        ws = [v for k, v in write if key in k]
+        if not fs:
+            continue
+        # the rewrite runs one launch per kind: a fold round is two dispatches
+        per = 2 if name.startswith("k_rewrite") else 1
+        rounds = len(fs) / per
+        fk, wk = sum(fs) / rounds, sum(ws) / rounds
+        # decode: the all-layer launches only (the one-layer calls come after the timed steps)
+        if name == "k_decode_unit":
+            big = sorted(fs)[-2:]
+            bigw = sorted(ws)[-2:]
+            fk, wk, rounds = sum(big) / 2, sum(bigw) / 2, 2
+        kern[name] = {"source": src,
+                      "source_sha256_16": source_hash(os.path.join(ROOT, "incremental_rank_svd_amd", "csrc", src)),
+                      "launches": int(rounds), "fetch_size_kib_avg": fk, "write_size_kib_avg": wk,
+                      "bytes_per_launch": 1024.0 * (fk * ff + wk * wf)}
+    out = {"workload": w.name, "coords": w.coord_dtype, "fetch_factor": ff, "write_factor": wf,
+           "calibration": "FETCH_SIZE and WRITE_SIZE of one elementwise copy kernel (bench.py --copy-calibration: "
+                          "1 GiB in, 1 GiB out) read %.1f and %.1f KiB" % (copy_f, copy_w),
+           "kernels": kern}
+    path = os.path.join(ROOT, "profiles", "traffic_%s%s.json" % (w.name, "_i8" if scale_b else ""))
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -584,6 +646,9 @@ def main():
         w = replace(w, layers=args.layers)
     if args.coords:
         w = replace(w, coord_dtype=args.coords)
+    if args.summarize_traffic:
+        summarize_traffic(args, w, 4 if w.coord_dtype == "i8" else 0)
+        return
     if not args.full_run:
         fold_decode_bench(args, w)
         return

@@ -132,7 +132,7 @@ size_t carve(const iskv_config *c, char *base, Layout *L) {
     // int8 rows are read in 16-byte pieces: keep every unit's rows 16-byte aligned
     s.cstride = l.coord_i8 ? ((size_t)l.ncap * r + 15) / 16 * 16 + 256 : (size_t)l.ncap * r + 256 / cb;
     s.C = take(U * s.cstride * cb);
-    s.cs = l.coord_i8 ? (float *)take(U * l.ncap * 4) : nullptr;
+    s.cs = l.coord_i8 ? (float *)take(U * cs_stride(l.ncap) * 4) : nullptr;
     s.Bt = (float *)take(U * r * D * 4);
     s.sig = (float *)take(U * r * 4);
     s.ring = take(U * l.rcap * D * kb);
@@ -675,7 +675,7 @@ static int copy_scales(iskv_t h, int which, int b, int layer, int head, float *o
   if (h->poisoned) return ISKV_ERR_POISONED;
   if (bad_unit(h, which, b, layer, head) || !h->L.coord_i8) return ISKV_ERR_ARG;
   const Stream &X = h->L.X[which];
-  float *sc = X.cs + (size_t)unit_index(h, b, layer, head) * h->L.ncap;
+  float *sc = X.cs + (size_t)unit_index(h, b, layer, head) * cs_stride(h->L.ncap);
   const size_t bytes = (size_t)h->n[layer] * 4;
   if (bytes == 0) return ISKV_OK;
   return fail_hip(h, out ? hipMemcpyAsync(out, sc, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream)

@@ -30,10 +30,14 @@ inline int scratch_rows(int block, int rank_k, int rank_v) {
   return pr > er ? pr : er;
 }
 
+// floats per unit of the int8 row scales: ncap rounded up to 4, so that four
+// consecutive rows' scales (from a multiple of 4) are one aligned 16-byte piece
+inline __host__ __device__ size_t cs_stride(int ncap) { return ((size_t)ncap + 3) & ~(size_t)3; }
+
 struct Stream {
   void *C;          // [U][cstride] coordinates C = U Sigma (coord dtype): ncap rows of r, zero beyond column k;
                     // int8 storage keeps U = C Sigma^-1 here as codes, one scale per row in cs
-  float *cs;        // [U][ncap] int8 storage: scale of each stored row of U (nullptr otherwise)
+  float *cs;        // [U][cs_stride(ncap)] int8 storage: scale of each stored row of U (nullptr otherwise)
   float *Bt;        // [U][r][D] basis vectors as rows, zero beyond row k
   float *sig;       // [U][r] singular values, zero beyond k
   void *ring;       // [U][rcap][D] exact window ring (kv dtype)
@@ -168,9 +172,20 @@ __device__ __forceinline__ float sum64(float v) {
 // int8 storage of a row of U: scale = max|u| / 127, code = round-half-even(u * 127 / max|u|),
 // the rounding decision taken in fp32 from the row's own maximum
 __device__ __forceinline__ float i8_inv_step(float m) { return m > 0.f ? 127.f / m : 0.f; }
+// (one rounding of v * inv to the nearest integer, ties to even, as in i8_pack4)
 __device__ __forceinline__ int i8_code(float v, float inv) {
-  const float q = rintf(v * inv);
-  return (int)fminf(fmaxf(q, -127.f), 127.f);
+  return (int)(int8_t)(__float_as_uint(fmaf(v, inv, 12582912.0f)) & 0xffu);
+}
+
+// Four codes packed into one dword (byte i = code of v_i), each the nearest
+// integer of v_i * inv, ties to even: one fma against 1.5 * 2^23 leaves that
+// integer in the low mantissa bits (|v_i * inv| <= 127.5 < 2^22), whose low
+// byte is the code in two's complement; two byte permutes gather them.
+__device__ __forceinline__ uint32_t i8_pack4(float v0, float v1, float v2, float v3, float inv) {
+  constexpr float MAGIC = 12582912.0f;
+  const uint32_t a = __float_as_uint(fmaf(v0, inv, MAGIC)), b = __float_as_uint(fmaf(v1, inv, MAGIC));
+  const uint32_t c = __float_as_uint(fmaf(v2, inv, MAGIC)), d = __float_as_uint(fmaf(v3, inv, MAGIC));
+  return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
 }
 
 // bf16 bits of a small integer (exact: |x| <= 256)
@@ -178,13 +193,16 @@ __device__ __forceinline__ uint32_t int_bf16(int x) { return __float_as_uint((fl
 
 // eight int8 codes (two dwords, low byte first) as eight bf16 values packed in
 // four dwords, the operand layout of the bf16 matrix-core instructions
+// (each byte flipped to q + 128, converted from its byte lane, less 128: exact;
+// the upper halves of two such floats are their bf16 values)
 __device__ __forceinline__ void i8x8_bf16(uint32_t w0, uint32_t w1, uint32_t out[4]) {
 #pragma unroll
-  for (int e = 0; e < 4; e++) {
-    const uint32_t w = e < 2 ? w0 : w1;
-    const int sh = 16 * (e & 1);
-    const int lo = ((int)(w << (24 - sh))) >> 24, hi = ((int)(w << (16 - sh))) >> 24;
-    out[e] = int_bf16(lo) | (int_bf16(hi) << 16);
+  for (int e = 0; e < 4; e += 2) {
+    const uint32_t w = (e == 0 ? w0 : w1) ^ 0x80808080u;
+    const float f0 = (float)(w & 0xffu) - 128.f, f1 = (float)((w >> 8) & 0xffu) - 128.f;
+    const float f2 = (float)((w >> 16) & 0xffu) - 128.f, f3 = (float)(w >> 24) - 128.f;
+    out[e] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    out[e + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
   }
 }
 

@@ -403,26 +403,51 @@ __device__ __forceinline__ void store_tile(uint16_t *tile, int ts, int rsV, int 
   }
 }
 
-// int8 storage: the same step over codes of U. Lane l takes the 8 codes of
-// columns 32 kc + 8 (l / 16) .. +7 of rows rb + l % 16 and rb + 16 + l % 16
-// (8 bytes each), the 32-row C_V tile is 32 rsV contiguous bytes read in
-// 16-byte pieces, and each lane takes the scales of the 8 rows its score
-// fragments hold (rows rb + 4 (l / 16) + i and rb + 16 + 4 (l / 16) + i);
-// rows at or past `we` get scale 0.
+// int8 storage: the same step over codes of U. The K order of the score
+// products is permuted so that lane l loads 16 contiguous codes of its rows
+// rb + l % 16 and rb + 16 + l % 16, columns 64 p + 16 (l / 16) .. +15 for each
+// whole pair p of K steps (step kc takes the half kc % 2 of pair kc / 2); a
+// last unpaired step (KS odd) loads 8 codes, columns 32 kc + 8 (l / 16) .. +7.
+// The q' fragments follow the same order. The 32-row C_V tile is 32 rsV contiguous
+// bytes read in 16-byte pieces, and each lane takes the scales of the 8 rows
+// its score fragments hold (rows rb + 4 (l / 16) + i and rb + 16 + 4 (l / 16)
+// + i); rows at or past `we` get scale 0.
+__device__ __forceinline__ u32x4_t load16_i8(const uint8_t *p, bool al16) {
+  if (al16) return *(const u32x4_t *)p;
+  const uint2 lo = *(const uint2 *)p, hi = *(const uint2 *)(p + 8);  // 8-byte aligned rows
+  return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
 template <int KS, int NV>
 __device__ __forceinline__ void load_step_i8(const uint8_t *CK, const uint8_t *CV, const float *sK,
                                              const float *sV, int rsK, int rsV, int rb, int we, int lane,
-                                             uint2 *ka, uint2 *kb, u32x4_t *vv, float *fk, float *fv) {
+                                             u32x4_t *ka, u32x4_t *kb, u32x4_t *vv, float *fk, float *fv) {
   const int hq = lane & 15, qd = lane >> 4;
+  const bool al16 = (rsK & 15) == 0;
+  constexpr int KP = (KS + 1) / 2;
 #pragma unroll
-  for (int kc = 0; kc < KS; kc++) {
-    const int col = kc * 32 + 8 * qd;
+  for (int p = 0; p < KP; p++) {
+    // a 16-code piece that starts below column rsK may end past it (rsK % 16
+    // == 8): the next row's codes then meet zero entries of q'
+    const bool single = 2 * p + 1 == KS;
+    const int col = single ? p * 64 + 8 * qd : p * 64 + 16 * qd;
     const int r0 = rb + hq, r1 = rb + 16 + hq;
-    ka[kc] = uint2{0u, 0u};
-    kb[kc] = uint2{0u, 0u};
+    ka[p] = u32x4_t{0u, 0u, 0u, 0u};
+    kb[p] = u32x4_t{0u, 0u, 0u, 0u};
     if (col < rsK) {
-      if (r0 < we) ka[kc] = *(const uint2 *)(CK + (size_t)r0 * rsK + col);
-      if (r1 < we) kb[kc] = *(const uint2 *)(CK + (size_t)r1 * rsK + col);
+      if (single) {
+        if (r0 < we) {
+          const uint2 v = *(const uint2 *)(CK + (size_t)r0 * rsK + col);
+          ka[p] = u32x4_t{v.x, v.y, 0u, 0u};
+        }
+        if (r1 < we) {
+          const uint2 v = *(const uint2 *)(CK + (size_t)r1 * rsK + col);
+          kb[p] = u32x4_t{v.x, v.y, 0u, 0u};
+        }
+      } else {
+        if (r0 < we) ka[p] = load16_i8(CK + (size_t)r0 * rsK + col, al16);
+        if (r1 < we) kb[p] = load16_i8(CK + (size_t)r1 * rsK + col, al16);
+      }
     }
   }
 #pragma unroll
@@ -434,11 +459,21 @@ __device__ __forceinline__ void load_step_i8(const uint8_t *CK, const uint8_t *C
     if (idx < 2 * rsV && rb + (16 * idx) / rsV < we)
       vv[z] = *(const u32x4_t *)(CV + (size_t)rb * rsV + 16 * idx);
   }
+  // rows rb + 4 qd .. +3 and rb + 16 + 4 qd .. +3: one aligned 16-byte piece
+  // each (rb and the per-unit scale stride are multiples of 4)
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int row = rb + ((i < 4) ? (4 * qd + i) : (16 + 4 * qd + i - 4));
-    fk[i] = row < we ? sK[row] : 0.f;
-    fv[i] = row < we ? sV[row] : 0.f;
+  for (int hf = 0; hf < 2; hf++) {
+    const int row = rb + 16 * hf + 4 * qd;
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (row < we) {
+      a = *(const f32x4_t *)(sK + row);
+      b = *(const f32x4_t *)(sV + row);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      fk[4 * hf + i] = row + i < we ? a[i] : 0.f;
+      fv[4 * hf + i] = row + i < we ? b[i] : 0.f;
+    }
   }
 }
 
@@ -702,15 +737,16 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   const uint16_t *CV = (const uint16_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
   const uint8_t *CK8 = (const uint8_t *)a.L.X[0].C + (size_t)u * a.L.X[0].cstride;
   const uint8_t *CV8 = (const uint8_t *)a.L.X[1].C + (size_t)u * a.L.X[1].cstride;
-  const float *sK = I8 ? a.L.X[0].cs + (size_t)u * a.L.ncap : nullptr;
-  const float *sV = I8 ? a.L.X[1].cs + (size_t)u * a.L.ncap : nullptr;
+  const float *sK = I8 ? a.L.X[0].cs + (size_t)u * cs_stride(a.L.ncap) : nullptr;
+  const float *sV = I8 ? a.L.X[1].cs + (size_t)u * cs_stride(a.L.ncap) : nullptr;
   // prefetching the next step doubles the load registers: only when they fit
   constexpr int NV = I8 ? (NTV + 1) / 2 : NTV;  // 16-byte pieces of the C_V tile per lane
   constexpr bool PF = I8 ? (NV + KS) <= 2 : (NTV + 2 * KS) <= 6;  // int8: 8 row scales per kind too
+  constexpr int KP = (KS + 1) / 2;  // int8: K-step pairs of 16-byte code pieces
   u32x4_t ka[KS], kb[KS], vv[NV];
-  uint2 ka8[KS], kb8[KS];
+  u32x4_t ka8[KP], kb8[KP];
   float fk[8], fv[8];
-  auto load = [&](int rb, u32x4_t *ka_, u32x4_t *kb_, uint2 *ka8_, uint2 *kb8_, u32x4_t *vv_, float *fk_,
+  auto load = [&](int rb, u32x4_t *ka_, u32x4_t *kb_, u32x4_t *ka8_, u32x4_t *kb8_, u32x4_t *vv_, float *fk_,
                   float *fv_) {
     if constexpr (I8)
       load_step_i8<KS, NV>(CK8, CV8, sK, sV, rsK, rsV, rb, we, lane, ka8_, kb8_, vv_, fk_, fv_);
@@ -756,7 +792,8 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const int col = kc * 32 + 8 * fd + i;
+      // int8 storage permutes the K order of whole step pairs (see load_step_i8)
+      const int col = (I8 && (kc | 1) < KS) ? 64 * (kc >> 1) + 16 * fd + 8 * (kc & 1) + i : kc * 32 + 8 * fd + i;
       x[i] = (fq < g && col < rsK) ? qsm[fq * rsK + col] : 0.f;
     }
     split8(x, frag[(kc * 2) * 64 + ln], frag[(kc * 2 + 1) * 64 + ln]);
@@ -785,7 +822,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       for (int rb = wb; rb < we; rb += 32) {
         const bool more = rb + 32 < we;
         u32x4_t nka[KS], nkb[KS], nvv[NV];
-        uint2 nka8[KS], nkb8[KS];
+        u32x4_t nka8[KP], nkb8[KP];
         float nfk[8], nfv[8];
         if constexpr (PF) {
           if (more) load(rb + 32, nka, nkb, nka8, nkb8, nvv, nfk, nfv);
@@ -797,10 +834,11 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
         if constexpr (I8) {
 #pragma unroll
           for (int kc = 0; kc < KS; kc++) {
+            const int pp = kc >> 1, hh = 2 * (kc & 1);
             uint32_t w[4];
-            i8x8_bf16(ka8[kc].x, ka8[kc].y, w);
+            i8x8_bf16(ka8[pp][hh], ka8[pp][hh + 1], w);
             ka[kc] = u32x4_t{w[0], w[1], w[2], w[3]};
-            i8x8_bf16(kb8[kc].x, kb8[kc].y, w);
+            i8x8_bf16(kb8[pp][hh], kb8[pp][hh + 1], w);
             kb[kc] = u32x4_t{w[0], w[1], w[2], w[3]};
           }
         }
@@ -869,8 +907,11 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
             for (int kc = 0; kc < KS; kc++) {
               ka[kc] = nka[kc];
               kb[kc] = nkb[kc];
-              ka8[kc] = nka8[kc];
-              kb8[kc] = nkb8[kc];
+            }
+#pragma unroll
+            for (int pp = 0; pp < KP; pp++) {
+              ka8[pp] = nka8[pp];
+              kb8[pp] = nkb8[pp];
             }
 #pragma unroll
             for (int i = 0; i < 8; i++) {

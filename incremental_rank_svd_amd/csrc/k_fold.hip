@@ -849,7 +849,7 @@ __device__ __forceinline__ void fold_body(const FoldArgs &a, float *smem) {
       Ht[(size_t)i * r + jr] = sn > 0.f ? tau[i] * Hn[(size_t)jr * sj + i] / sn : 0.f;
     }
     int8_t *Cn = (int8_t *)X.C + (size_t)u * X.cstride + (size_t)a.n * r;
-    float *cs = X.cs + (size_t)u * a.ncap + a.n;
+    float *cs = X.cs + (size_t)u * cs_stride(a.ncap) + a.n;
     const int wv = tid >> 6, ln = tid & 63;
     for (int i = wv; i < b; i += NW) {
       float v[2];

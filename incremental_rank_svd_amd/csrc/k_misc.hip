@@ -188,7 +188,7 @@ hipError_t launch_reconstruct(const Layout &L, int which, int u, int n, int k, i
   const size_t roff = (size_t)u * L.rcap * D;
   if (L.coord_i8) {
     hipLaunchKernelGGL(k_reconstruct_i8, dim3(rows), dim3(NT), 0, s, Bt, (const int8_t *)X.C + coff,
-                       X.cs + (size_t)u * L.ncap, X.sig + (size_t)u * X.r, (const uint16_t *)X.ring + roff, X.r,
+                       X.cs + (size_t)u * cs_stride(L.ncap), X.sig + (size_t)u * X.r, (const uint16_t *)X.ring + roff, X.r,
                        n, k, e, head, L.rcap, out);
     return hipGetLastError();
   }

@@ -296,11 +296,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int u = a.u0 + blockIdx.y;
   const float *Ht = X.Htop + (size_t)u * r * r;
-  // fragment (t, s, part) of lane l: M[32s + 8(l/16) + e][16t + l%16], e < 8
+  // The K order of the products is permuted so that lane l loads 16
+  // contiguous codes, columns 64 p + 16 (l / 16) .. +15 of its row, for each
+  // whole pair p of K steps (whole 16-row groups per load instruction): step
+  // s takes the half s % 2 of pair s / 2. A last unpaired step (S odd) loads
+  // 8 codes, columns 32 s + 8 (l / 16) .. +7. The fragments of M follow the
+  // same order: fragment (t, s, part) of lane l holds M[kb + e][16t + l%16],
+  // e < 8, kb = 64 (s/2) + 16 (l/16) + 8 (s%2) in a pair, else 32 s + 8 (l/16).
   for (int f = wv; f < T * S; f += NT / 64) {
     const int t = f / S, s = f - t * S;
     const int j = 16 * t + (lane & 15);
-    const int kb = 32 * s + 8 * (lane >> 4);
+    const int kb = (s | 1) < S ? 64 * (s >> 1) + 16 * (lane >> 4) + 8 * (s & 1) : 32 * s + 8 * (lane >> 4);
     uint32_t w0[4], w1[4], w2[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -324,7 +330,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
   }
   __syncthreads();
   int8_t *C = (int8_t *)X.C + (size_t)u * X.cstride;
-  float *cs = X.cs + (size_t)u * a.ncap;
+  float *cs = X.cs + (size_t)u * cs_stride(a.ncap);
   const int ngroups = (a.n + 15) / 16;
   const int gstride = gridDim.x * (NT / 64);
   // codes and scales through buffer resources whose ranges are the n stored
@@ -333,8 +339,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, a.n * r, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(cs, (short)0, a.n * 4, 0x00020000);
   constexpr uint32_t OUT = 0x80000000u;
-  const int kq = 8 * (lane >> 4), jq = 4 * (lane >> 4);
-  auto coff = [&](int s) { return 32 * s + kq < r ? (uint32_t)(32 * s + kq) : OUT; };
+  const int jq = 4 * (lane >> 4);
+  constexpr int SP = (SM + 1) / 2;  // K-step pairs (the last one may be a single step)
+  // column of lane l's piece of pair p: 16 codes in a whole pair, 8 in a last single step
+  // (a 16-code piece that starts below column r may end past it when r % 16 == 8:
+  // those codes belong to the next row and meet rows of M past k, which are zero)
+  auto pcol = [&](int p) { return 2 * p + 1 < S ? 64 * p + 16 * (lane >> 4) : 64 * p + 8 * (lane >> 4); };
+  auto coff = [&](int p) { return pcol(p) < r ? (uint32_t)pcol(p) : OUT; };
+  const bool al16 = (r & 15) == 0;  // 16-byte pieces are 16-byte aligned
   constexpr int GB = 16 * 16 * T;             // bytes of a group's staging (16 rows of at most 16 T)
   constexpr int NI = (GB + 1023) / 1024;      // 16-byte pieces per lane
   char *stg = reinterpret_cast<char *>(fr + (size_t)T * S * HP * 64) + wv * GB;
@@ -346,18 +358,33 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
     sl[i] = off < 16 * r ? (uint32_t)off : 0u;
     so[i] = off < 16 * r ? (uint32_t)off : OUT;
   }
-  auto load_groups = [&](int g0, u32x2v_t (&cf)[RG][SM], float (&sc)[RG]) {
+  auto load_groups = [&](int g0, u32x4_t (&cf)[RG][SP], float (&sc)[RG]) {
 #pragma unroll
     for (int q = 0; q < RG; q++) {
       const uint32_t row = (uint32_t)((g0 + q * gstride) * 16 + (lane & 15));
       const uint32_t ro = row * (uint32_t)r;
 #pragma unroll
-      for (int s = 0; s < SM; s++)
-        cf[q][s] = s < S ? __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(ro + coff(s)), 0, 0) : u32x2v_t{0u, 0u};
+      for (int p = 0; p < SP; p++) {
+        if (2 * p + 1 == S) {  // last single step: 8 codes
+          const u32x2v_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(ro + coff(p)), 0, 0);
+          cf[q][p] = u32x4_t{lo[0], lo[1], 0u, 0u};
+        } else if (2 * p < S) {
+          const int o = (int)(ro + coff(p));
+          if (al16) {
+            cf[q][p] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+          } else {
+            const u32x2v_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+            const u32x2v_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs, o + 8, 0, 0);
+            cf[q][p] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+        } else {
+          cf[q][p] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
       sc[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(row * 4u), 0, 0));
     }
   };
-  u32x2v_t cf[RG][SM], cn[RG][SM];
+  u32x4_t cf[RG][SP], cn[RG][SP];
   float sc[RG], scn[RG];
   const int gfirst = blockIdx.x * (NT / 64) + wv;
   if (gfirst < ngroups) load_groups(gfirst, cn, scn);
@@ -367,10 +394,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
     for (int q = 0; q < RG; q++) {
       sc[q] = scn[q];
 #pragma unroll
+      for (int p = 0; p < SP; p++) cf[q][p] = cn[q][p];
+#pragma unroll
       for (int s = 0; s < SM; s++) {
-        cf[q][s] = cn[q][s];
         uint32_t w[4];
-        i8x8_bf16(cf[q][s][0], cf[q][s][1], w);
+        i8x8_bf16(cf[q][s >> 1][2 * (s & 1)], cf[q][s >> 1][2 * (s & 1) + 1], w);
         bq[q][s] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
     }
@@ -406,12 +434,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
       const float inv = i8_inv_step(m);
 #pragma unroll
       for (int t = 0; t < T; t++) {
-        if (16 * t + jq < r) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int i = 0; i < 4; i++) w |= ((uint32_t)i8_code(ob[q][t][i], inv) & 0xffu) << (8 * i);
-          *reinterpret_cast<uint32_t *>(stw + 16 * t) = w;
-        }
+        if (16 * t + jq < r)
+          *reinterpret_cast<uint32_t *>(stw + 16 * t) =
+              i8_pack4(ob[q][t][0], ob[q][t][1], ob[q][t][2], ob[q][t][3], inv);
       }
       // other lanes of this wave read what it wrote (a wave's LDS accesses
       // complete in order; the fences keep the compiler from moving them)
@@ -736,7 +761,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
   }
   __syncthreads();
   // pass 2: rows of U in int8 with per-row scales
-  float *scl = X.cs + (size_t)u * a.ncap;
+  float *scl = X.cs + (size_t)u * cs_stride(a.ncap);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(scl, (short)0, a.nrows * 4, 0x00020000);
   float iv[T][4];
 #pragma unroll
@@ -767,12 +792,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) k_
       const float inv = i8_inv_step(m);
 #pragma unroll
       for (int t = 0; t < T; t++) {
-        if (16 * t + jq < r) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int v = 0; v < 4; v++) w |= ((uint32_t)i8_code(ob[q][t][v], inv) & 0xffu) << (8 * v);
-          *reinterpret_cast<uint32_t *>(stw + 16 * t) = w;
-        }
+        if (16 * t + jq < r)
+          *reinterpret_cast<uint32_t *>(stw + 16 * t) =
+              i8_pack4(ob[q][t][0], ob[q][t][1], ob[q][t][2], ob[q][t][3], inv);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       const uint32_t grow = (uint32_t)(g0 + q * gstride) * 16u;
