@@ -8,7 +8,13 @@ fp64 oracle runs exactly those rows one unit at a time. Gates:
   * bf16 coordinates (the storage the benchmark times): decode attention on
     the stored factors (2e-3), rank sequence identical, no numeric flags; the
     distance of the bf16 history to the fp64 oracle is reported and bounded
-    by the bf16 re-rounding random walk, sqrt(folds) * 2^-8.
+    by the bf16 re-rounding random walk, sqrt(folds) * 2^-8;
+  * int8 coordinates (codes of U, one scale per row): decode on the stored
+    factors (2e-3), rank sequence identical, no numeric flags, every stored
+    row on its own int8 grid, and the history within the summed per-fold
+    storage bounds (half a step per entry of U, times sigma) of the fp64
+    oracle, its error against the true rows within that of the oracle plus
+    the same bound.
 The long-input and 13B-MHA workloads keep their full per-unit sizes; the
 MHA one runs 2 of its 40 layers (units are independent).
 """
@@ -145,6 +151,67 @@ def _bf16_case(iskv, w, samples, per_token=False):
         w.name, worst, bound, max(derrs), folds))
 
 
+def _i8_state(cache, which, b, l, h):
+    C, sig, Bt, W = cache.export_state(which, b, l, h)
+    sc = cache.export_scales(which, b, l, h).cpu().double().numpy()
+    n, e, kk, kv = cache.counts(l)
+    k = kk if which == 0 else kv
+    q = C.cpu().numpy().astype(np.int64)
+    sg = sig.cpu().double().numpy()
+    return q, sc, sg, Bt.cpu().double().numpy(), W.float().cpu().double().numpy(), n, e, k
+
+
+def _i8_case(iskv, w, samples, per_token=False):
+    cache, host, seq = _run(iskv, w, "i8", samples, per_token=per_token)
+    assert cache.status() == 0
+    ora = _oracle(w, host, samples)
+    folds = len(seq)
+    worst = 0.0
+    recs = {}
+    for smp in samples:
+        _check_ranks(seq, {x: ora[(x, smp)] for x in "KV"})
+        for which, x in ((0, "K"), (1, "V")):
+            q, sc, sg, Bt, W, n, e, k = _i8_state(cache, which, *smp)
+            assert np.all(np.abs(q) <= 127) and np.all(q[:, k:] == 0)
+            m = np.abs(q[:, :k]).max(axis=1)
+            assert np.all((m == 127) | ((m == 0) & (sc == 0)))  # each row reaches its own scale
+            C = q[:, :k] * sc[:, None] * sg[:k]
+            rec = oracle.reconstruct(C, Bt[:k], W, k=k)
+            got = cache.reconstruct(which, *smp).cpu().double().numpy()
+            assert np.linalg.norm(got - rec) <= 1e-5 * np.linalg.norm(rec)
+            recs[(x, smp)] = rec
+            # per-fold storage bound: half a step on each entry of U, times sigma
+            step = np.linalg.norm(sc[:, None] * 0.5 * sg[:k]) / np.linalg.norm(C)
+            bound = folds * step
+            ref = ora[(x, smp)].reconstruct()
+            Xt = host[(x,) + smp][: n + e]
+            rel = float(np.linalg.norm(rec - ref) / np.linalg.norm(ref))
+            assert rel <= bound, (smp, x, rel, bound)
+            eg = np.linalg.norm(rec - Xt) / np.linalg.norm(Xt)
+            eo = np.linalg.norm(ref - Xt) / np.linalg.norm(Xt)
+            assert eg <= eo + bound, (smp, x, eg, eo, bound)
+            worst = max(worst, rel)
+    tdt = torch.bfloat16
+    g = w.group
+    derr = 0.0
+    for step in range(2):
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(4321 + step)
+        qd = torch.randn((w.batch, w.layers, w.q_heads, D), generator=gen, device=DEV).to(tdt)
+        hostq = {}
+        for (b, l, h) in samples:
+            qs = synth.queries(w, step, b, l)
+            hostq[(b, l)] = qs
+            qd[b, l] = torch.tensor(qs, dtype=torch.float32, device=DEV).to(tdt)
+        out = cache.decode_attn(qd).cpu().double().numpy()
+        for (b, l, h) in samples:
+            ref = oracle.attend(recs[("K", (b, l, h))], recs[("V", (b, l, h))], hostq[(b, l)][h * g:(h + 1) * g],
+                                D ** -0.5)
+            derr = max(derr, decode_err(out[b, l, h * g:(h + 1) * g], ref))
+    assert derr <= DEC_TOL, derr
+    note("  %s int8 coords: history vs fp64 oracle %.2e, decode %.2e, folds %d" % (w.name, worst, derr, folds))
+
+
 def test_llama3_8b_bench_configuration_bf16(iskv):
     """The benchmark's launch configuration: every token appended to all 32
     layers one at a time, bf16 storage, then decode on sampled units."""
@@ -181,3 +248,19 @@ def test_llama2_13b_mha_unit_sizes(iskv, coord):
     note("case: %s (2 layers) %s" % (w.name, coord))
     samples = [(15, 1, 39), (4, 0, 11)]
     (_fp32_case if coord == "f32" else _bf16_case)(iskv, w, samples)
+
+
+def test_int8_coordinates_llama3_8b_per_token(iskv):
+    """The 8B-GQA workload with int8 storage, every token appended to all 32
+    layers one at a time (the full-run launch configuration)."""
+    w = synth.get_config(1)
+    note("case: %s int8, per-token appends" % w.name)
+    _i8_case(iskv, w, [(0, 0, 0), (0, 31, 7)], per_token=True)
+
+
+def test_int8_coordinates_llama2_13b_mha_unit_sizes(iskv):
+    """The 13B-MHA workload's full per-unit length (16384 tokens, b = 128,
+    ranks 64 / 96) with int8 storage, 2 of its 40 layers."""
+    w = replace(synth.get_config(4), layers=2)
+    note("case: %s (2 layers) int8" % w.name)
+    _i8_case(iskv, w, [(15, 1, 39), (4, 0, 11)])
