@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--coords", choices=("f32", "bf16", "i8"), default=None,
                    help="stored coordinate type (default: the workload's); i8 = int8 codes of U with "
                         "one fp32 scale per row")
+    p.add_argument("--decode-snapshots", default="",
+                   help="comma-separated history lengths: inject each state by one-shot prefill and time "
+                        "decode only (all layers) there, one JSON line")
     p.add_argument("--summarize-traffic", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                    help="write profiles/traffic_<workload>[_i8].json from four rocprofv3 --pmc output "
                         "folders (copy calibration FETCH_SIZE, WRITE_SIZE; bench FETCH_SIZE, WRITE_SIZE)")
@@ -562,6 +565,74 @@ def prefill_bench(args):
     }), flush=True)
 
 
+def decode_snapshots(args, w):
+    """Decode-only rate at several history lengths n: per n the cache is
+    reset, every layer's first n rows are factorised by iskv_prefill_oneshot
+    (device-generated rows of the workload's distribution), the window is
+    filled to w rows, then the median of 20 all-layer iskv_decode_attn
+    launches (HIP events on the launch stream) gives GB/s against the
+    algorithmic bytes of the launch."""
+    import numpy as np
+    import torch
+
+    import synth
+    from incremental_rank_svd_amd import iskv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = iskv.load()
+    B, L, Hk, Hq, b, wnd = w.batch, w.layers, w.kv_heads, w.q_heads, w.block, w.window
+    U = B * L * Hk
+    kv_b = 2
+    coord_b = {"bf16": 2, "f32": 4, "i8": 1}[w.coord_dtype]
+    scale_b = 4 if w.coord_dtype == "i8" else 0
+    ns = [int(x) for x in args.decode_snapshots.split(",")]
+    cache = iskv.Cache(iskv.config_from_workload(w), device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    VP = ctypes.c_void_p
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    Q = torch.randn((B, L, Hq, 128), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, L, Hq, 128), dtype=torch.float32, device=dev)
+    scale = ctypes.c_float(128 ** -0.5)
+    snaps = []
+    for n in ns:
+        n = min(n, w.max_tokens - wnd) // b * b
+        cache.reset()
+        for l in range(L):
+            rows = {x: synth.kv_rows_device(w, x, n + wnd, dev, layer0=l, nlayers=1) for x in "KV"}
+            cache.prefill_oneshot(rows["K"][:, :, :, :n].contiguous(), rows["V"][:, :, :, :n].contiguous(), layer0=l)
+            for s0 in range(0, wnd, b):
+                s1 = min(wnd, s0 + b)
+                cache.append_block(rows["K"][:, :, :, n + s0:n + s1].contiguous(),
+                                   rows["V"][:, :, :, n + s0:n + s1].contiguous(), layer0=l)
+            del rows
+        torch.cuda.synchronize()
+        nn, e, kK, kV = cache.counts(0)
+        evs = []
+        for i in range(22):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            if lib.iskv_decode_attn(cache.h, VP(Q.data_ptr()), VP(out.data_ptr()), 0, L, scale, sp):
+                raise RuntimeError("decode_attn failed")
+            a1.record(stream)
+            evs.append((a0, a1))
+        torch.cuda.synchronize()
+        if cache.status():
+            raise RuntimeError("numeric flags after the snapshot at n = %d" % n)
+        ms = float(np.median([a.elapsed_time(c) for a, c in evs[2:]]))
+        byts = decode_bytes(U, w.group, nn, e, kK, kV, coord_b, kv_b, scale_b=scale_b)
+        snaps.append({"n": nn, "e": e, "k_k": kK, "k_v": kV, "state_GB": U * nn * (kK + kV) * coord_b / 1e9,
+                      "ms": ms, "GBps": byts / (ms * 1e-3) / 1e9, "frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "tokens_per_s": B / (ms * 1e-3)})
+        print("snapshot n = %d: %.3f ms, %.0f GB/s" % (nn, ms, snaps[-1]["GBps"]), file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "decode-attn tokens/sec and % of HBM roofline at fixed history lengths",
+                      "workload": w.name, "coords": w.coord_dtype, "units": U, "window": wnd,
+                      "kernel": "k_decode_unit", "snapshots": snaps}), flush=True)
+
+
 def _pmc_rows(folder):
     """(kernel name, counter value) of every dispatch in a rocprofv3 --pmc csv folder."""
     import csv
@@ -648,6 +719,9 @@ def main():
         w = replace(w, coord_dtype=args.coords)
     if args.summarize_traffic:
         summarize_traffic(args, w, 4 if w.coord_dtype == "i8" else 0)
+        return
+    if args.decode_snapshots:
+        decode_snapshots(args, w)
         return
     if not args.full_run:
         fold_decode_bench(args, w)
