@@ -183,8 +183,8 @@ ISKV_API int iskv_decode_attn(iskv_t h, const void *q, float *out, int32_t layer
  * ISKV_STATIC_SCRATCH_BYTES owned by the library, one per GPU, held until the
  * process ends; nothing in it needs clearing (each call writes every partial
  * it reads). Calls that overlap on one GPU (any handle, any stream) race on
- * that array: serialize them. Requires bf16 coordinates and rows and ranks
- * that are multiples of 8 (else ISKV_ERR_ARG); a call whose partials exceed
+ * that array: serialize them. Requires bf16 or int8 (ISKV_I8) coordinates,
+ * bf16 rows and ranks that are multiples of 8 (else ISKV_ERR_ARG); a call whose partials exceed
  * the array (units x splits x g x (2 + r_V + d) floats, at least one split per
  * unit) returns ISKV_ERR_SCRATCH; ISKV_ERR_HIP if the array's device address
  * could not be obtained at iskv_init. All checks happen before anything is
