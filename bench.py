@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--sample-every", type=int, default=1,
                    help="event-time every n-th run of decode launches between two folds")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-int8", action="store_true", help="skip the int8-coordinate variant of the default step")
     p.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (unit streams)")
     p.add_argument("--prefill", action="store_true",
                    help="time the one-shot prompt factorisation of the long-input workload against "
@@ -277,7 +278,27 @@ def cpu_baseline_fold_decode(w, n0, nunits):
 
 
 def fold_decode_bench(args, w):
-    """One fold round plus one decode step per step, at the end of the run."""
+    """One fold round plus one decode step per step, at the end of the run;
+    with the workload's own bf16 coordinates the same step is then timed
+    again with int8 coordinates (the bf16 state freed first) and attached as
+    `int8_coordinates`."""
+    import torch
+    from dataclasses import replace
+
+    res, n_mid = fold_decode_step(args, w)
+    if w.coord_dtype == "bf16" and args.coords is None and not args.no_int8:
+        torch.cuda.empty_cache()
+        r8, _ = fold_decode_step(args, replace(w, coord_dtype="i8"))
+        res["int8_coordinates"] = {k: r8[k] for k in ("value", "unit", "ms_per_step", "dtype", "decode_attn_tokens_per_s",
+                                                      "kernel_ms", "roofline_kernels", "decode_one_layer")}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_fold_decode(w, n_mid, args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+def fold_decode_step(args, w):
+    """The measurement of fold_decode_bench for one coordinate type; returns
+    (result dict, history rows at the middle of the timed steps)."""
     import numpy as np
     import torch
 
@@ -452,11 +473,9 @@ def fold_decode_bench(args, w):
     # decode of one layer per call, as a model's layer loop issues it (after the timed region)
     res["decode_one_layer"] = one_layer_decode(lib, h, Q[-1], out, L, B, Hk, Hq, n_fin, wnd, kK, kV, w.group,
                                                coord_b, kv_b, stream, sp, scale_b=scale_b)
-    print("timed: %d steps, %.1f ms per step" % (args.steps, step_s * 1e3), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_fold_decode(w, n0 + (args.warmup + args.steps // 2) * b,
-                                                       args.cpu_units)
-    print(json.dumps(res), flush=True)
+    print("timed (%s coordinates): %d steps, %.1f ms per step" % (w.coord_dtype, args.steps, step_s * 1e3),
+          file=sys.stderr, flush=True)
+    return res, n0 + (args.warmup + args.steps // 2) * b
 
 
 def one_layer_decode(lib, h, q, out, L, B, Hk, Hq, n, e, kK, kV, g, coord_b, kv_b, stream, sp, reps=50,
