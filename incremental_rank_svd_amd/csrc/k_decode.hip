@@ -742,6 +742,9 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
   // prefetching the next step doubles the load registers: only when they fit
   constexpr int NV = I8 ? (NTV + 1) / 2 : NTV;  // 16-byte pieces of the C_V tile per lane
   constexpr bool PF = I8 ? (NV + KS) <= 2 : (NTV + 2 * KS) <= 6;  // int8: 8 row scales per kind too
+  // int8 at small ranks: 64-row steps of two loaded halves instead of a
+  // prefetched 32-row step (measured: 8-10% faster there; no gain for bf16)
+  constexpr bool TWO = I8 && PF && KS == 1;
   constexpr int KP = (KS + 1) / 2;  // int8: K-step pairs of 16-byte code pieces
   u32x4_t ka[KS], kb[KS], vv[NV];
   u32x4_t ka8[KP], kb8[KP];
@@ -814,23 +817,10 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       else
         store_tile<NTV>(tile, ts, rsV, lane, vv_);
     };
-    if (wb < we) {
-      if constexpr (PF) {
-        put_tile(wb, vv);
-        wave_fence();
-      }
-      for (int rb = wb; rb < we; rb += 32) {
-        const bool more = rb + 32 < we;
-        u32x4_t nka[KS], nkb[KS], nvv[NV];
-        u32x4_t nka8[KP], nkb8[KP];
-        float nfk[8], nfv[8];
-        if constexpr (PF) {
-          if (more) load(rb + 32, nka, nkb, nka8, nkb8, nvv, nfk, nfv);
-        } else {
-          load(rb, ka, kb, ka8, kb8, vv, fk, fv);
-          put_tile(rb, vv);
-          wave_fence();
-        }
+    // one 32-row step over registers loaded by `load` (its C_V tile already in
+    // the wave's LDS tile): scores, online softmax, weighted values
+    auto compute = [&](int rb, u32x4_t *ka, u32x4_t *kb, const u32x4_t *ka8, const u32x4_t *kb8, const float *fk,
+                       const float *fv) {
         if constexpr (I8) {
 #pragma unroll
           for (int kc = 0; kc < KS; kc++) {
@@ -899,6 +889,47 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
           acc[nt] = mfma16(av, phi, acc[nt]);
           acc[nt] = mfma16(av, plo, acc[nt]);
         }
+    };
+    if (wb < we) {
+      if constexpr (TWO) {
+        // small ranks: both halves of a 64-row step are loaded at once, so one
+        // memory latency serves 64 rows (the second half's loads are issued
+        // even when it is empty: every lane's rows are then past we and masked)
+        for (int rb = wb; rb < we; rb += 64) {
+          u32x4_t nka[KS], nkb[KS], nvv[NV];
+          u32x4_t nka8[KP], nkb8[KP];
+          float nfk[8], nfv[8];
+          load(rb, ka, kb, ka8, kb8, vv, fk, fv);
+          load(rb + 32, nka, nkb, nka8, nkb8, nvv, nfk, nfv);
+          put_tile(rb, vv);
+          wave_fence();
+          compute(rb, ka, kb, ka8, kb8, fk, fv);
+          wave_fence();
+          if (rb + 32 < we) {
+            put_tile(rb + 32, nvv);
+            wave_fence();
+            compute(rb + 32, nka, nkb, nka8, nkb8, nfk, nfv);
+            wave_fence();
+          }
+        }
+      } else {
+      if constexpr (PF) {
+        put_tile(wb, vv);
+        wave_fence();
+      }
+      for (int rb = wb; rb < we; rb += 32) {
+        const bool more = rb + 32 < we;
+        u32x4_t nka[KS], nkb[KS], nvv[NV];
+        u32x4_t nka8[KP], nkb8[KP];
+        float nfk[8], nfv[8];
+        if constexpr (PF) {
+          if (more) load(rb + 32, nka, nkb, nka8, nkb8, nvv, nfk, nfv);
+        } else {
+          load(rb, ka, kb, ka8, kb8, vv, fk, fv);
+          put_tile(rb, vv);
+          wave_fence();
+        }
+        compute(rb, ka, kb, ka8, kb8, fk, fv);
         wave_fence();
         if constexpr (PF) {
           if (more) {
@@ -921,6 +952,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
           }
           wave_fence();
         }
+      }
       }
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
