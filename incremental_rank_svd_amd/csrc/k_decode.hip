@@ -297,16 +297,23 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+// two fp32 values to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // x = hi + lo with both parts bf16 (round to nearest even)
 __device__ __forceinline__ void split8(const float *x, u32x4_t &hi, u32x4_t &lo) {
-  uint16_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    h[i] = f2bf(x[i]);
-    l[i] = f2bf(x[i] - bf2f(h[i]));
+  for (int i = 0; i < 4; i++) {
+    h[i] = cvt_pk_bf16(x[2 * i], x[2 * i + 1]);
+    l[i] = cvt_pk_bf16(x[2 * i] - __uint_as_float(h[i] << 16), x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
   }
-  hi = u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-  lo = u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+  hi = u32x4_t{h[0], h[1], h[2], h[3]};
+  lo = u32x4_t{l[0], l[1], l[2], l[3]};
 }
 
 __device__ __forceinline__ void wave_fence() {
@@ -500,6 +507,12 @@ __device__ __forceinline__ void store_tile_i8(uint16_t *tile, int ts, int rsV, i
   }
 }
 
+// The matrix-core decode keeps its scores in base-2 units (scale * log2(e)
+// folded into q' and the window scores), so every softmax weight, rescale
+// and merge factor is one v_exp_f32.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Window rows of one unit straight from the ring (used when the window does
 // not fit in LDS): row i goes to lane group (i mod 64) of the workgroup (16
 // lanes per 128-wide row), WH heads per pass, online softmax; the 4 lane
@@ -518,7 +531,7 @@ __device__ __forceinline__ void window_part(const DecodeArgs &a, const uint16_t 
 #pragma unroll
       for (int t = 0; t < 8; t++) {
         wa[j][t] = 0.f;
-        qv[j][t] = (h0 + j < g) ? a.scale * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
+        qv[j][t] = (h0 + j < g) ? a.scale * LOG2E * bf2f(q[(size_t)(h0 + j) * D + l16 * 8 + t]) : 0.f;
       }
     }
     for (int i = gg; i < a.e; i += 4 * NWU) {
@@ -539,8 +552,8 @@ __device__ __forceinline__ void window_part(const DecodeArgs &a, const uint16_t 
         for (int t = 0; t < 8; t++) sc += kx[t] * qv[j][t];
         sc = sum16(sc);
         const float mn = fmaxf(wm[j], sc);
-        const float al = __expf(wm[j] - mn);
-        const float pv = __expf(sc - mn);
+        const float al = ex2(wm[j] - mn);
+        const float pv = ex2(sc - mn);
         wl[j] = wl[j] * al + pv;
 #pragma unroll
         for (int t = 0; t < 8; t++) wa[j][t] = wa[j][t] * al + pv * vx[t];
@@ -556,7 +569,7 @@ __device__ __forceinline__ void window_part(const DecodeArgs &a, const uint16_t 
         const float lo = __shfl_xor(wl[j], off);
         const float mn = fmaxf(wm[j], mo);
         const float ms = (mn == -INFINITY) ? 0.f : mn;
-        const float f0 = __expf(wm[j] - ms), f1 = __expf(mo - ms);
+        const float f0 = ex2(wm[j] - ms), f1 = ex2(mo - ms);
         wl[j] = wl[j] * f0 + lo * f1;
 #pragma unroll
         for (int t = 0; t < 8; t++) {
@@ -611,8 +624,8 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u3
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      s[i] = (rb + 4 * qd + i < e) ? a.scale * d0[i] : -INFINITY;
-      s[4 + i] = (rb + 16 + 4 * qd + i < e) ? a.scale * d1[i] : -INFINITY;
+      s[i] = (rb + 4 * qd + i < e) ? (a.scale * LOG2E) * d0[i] : -INFINITY;
+      s[4 + i] = (rb + 16 + 4 * qd + i < e) ? (a.scale * LOG2E) * d1[i] : -INFINITY;
     }
     float mx = s[0];
 #pragma unroll
@@ -621,11 +634,11 @@ __device__ __forceinline__ void window_mfma(const DecodeArgs &a, int e, const u3
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(m, mx);
     const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float al = __expf(m - ms);
+    const float al = ex2(m - ms);
     float p[8], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      p[i] = __expf(s[i] - ms);
+      p[i] = ex2(s[i] - ms);
       ps += p[i];
     }
     l = l * al + ps;
@@ -757,7 +770,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       load_step<KS, NTV>(CK, CV, rsK, rsV, rb, we, lane, ka_, kb_, vv_);
   };
   if (PF && wb < we) load(wb, ka, kb, ka8, kb8, vv, fk, fv);
-  // q' = scale * B_K^T q, zero beyond the current rank (16 lanes per dot)
+  // q' = scale * log2(e) * B_K^T q, zero beyond the current rank (16 lanes per dot)
   {
     const float *Bt = a.L.X[0].Bt + (size_t)u * rsK * D;
     const int l16 = tid & 15, grp = tid >> 4;
@@ -770,7 +783,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
       }
       s = sum16(s);
       if constexpr (I8) s *= (jj < a.kK) ? a.L.X[0].sig[(size_t)u * rsK + jj] : 0.f;  // Sigma_K q'
-      if (l16 == 0) qsm[hh * rsK + jj] = a.scale * s;
+      if (l16 == 0) qsm[hh * rsK + jj] = (a.scale * LOG2E) * s;
     }
   }
   if (a.wlds && tid < 4 * 64) {
@@ -842,12 +855,20 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
           d1 = mfma16(kb[kc], bl, d1);
         }
         float s[8];
+        if (rb + 32 <= we) {  // a whole step (all but a wave's last): no row past we
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          // int8 storage: each row's score takes its scale
-          const float f0 = I8 ? fk[i] : 1.f, f1 = I8 ? fk[4 + i] : 1.f;
-          s[i] = (rb + 4 * qd + i < we) ? d0[i] * f0 : -INFINITY;
-          s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] * f1 : -INFINITY;
+          for (int i = 0; i < 4; i++) {
+            // int8 storage: each row's score takes its scale
+            s[i] = I8 ? d0[i] * fk[i] : d0[i];
+            s[4 + i] = I8 ? d1[i] * fk[4 + i] : d1[i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float f0 = I8 ? fk[i] : 1.f, f1 = I8 ? fk[4 + i] : 1.f;
+            s[i] = (rb + 4 * qd + i < we) ? d0[i] * f0 : -INFINITY;
+            s[4 + i] = (rb + 16 + 4 * qd + i < we) ? d1[i] * f1 : -INFINITY;
+          }
         }
         float mx = s[0];
 #pragma unroll
@@ -856,11 +877,11 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(m, mx);
         const float ms = (mn == -INFINITY) ? 0.f : mn;
-        const float al = __expf(m - ms);
+        const float al = ex2(m - ms);
         float p[8], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          p[i] = __expf(s[i] - ms);
+          p[i] = ex2(s[i] - ms);
           ps += p[i];
         }
         l = l * al + ps;
@@ -1011,10 +1032,10 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     for (int w = 0; w < nwo; w++) M = fmaxf(M, wo[((size_t)w * g + tid) * (2 + D)]);
     const float ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
-    for (int w = 0; w < NWU; w++) L += __expf(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
+    for (int w = 0; w < NWU; w++) L += ex2(hm[w * MAXG + tid] - ms) * hl[w * MAXG + tid];
     for (int w = 0; w < nwo; w++) {
       const float *ww = wo + ((size_t)w * g + tid) * (2 + D);
-      L += __expf(ww[0] - ms) * ww[1];
+      L += ex2(ww[0] - ms) * ww[1];
     }
     fac[tid * 8 + 0] = ms;
     fac[tid * 8 + 1] = L;
@@ -1024,7 +1045,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     const int hh = idx / rsV, j = idx - hh * rsV;
     const float ms = fac[hh * 8];
     float s = 0.f;
-    for (int w = 0; w < NWU; w++) s += __expf(hm[w * MAXG + hh] - ms) * ha[((size_t)w * g + hh) * rsV + j];
+    for (int w = 0; w < NWU; w++) s += ex2(hm[w * MAXG + hh] - ms) * ha[((size_t)w * g + hh) * rsV + j];
     op[idx] = s;
   }
   for (int idx = tid; idx < g * D; idx += NTU) {
@@ -1033,7 +1054,7 @@ __global__ void __launch_bounds__(NTU) k_decode_unit(const DecodeArgs a) {
     float s = 0.f;
     for (int w = 0; w < nwo; w++) {
       const float *ww = wo + ((size_t)w * g + hh) * (2 + D);
-      s += __expf(ww[0] - ms) * ww[2 + t];
+      s += ex2(ww[0] - ms) * ww[2 + t];
     }
     ow[idx] = s;
   }
@@ -1104,7 +1125,7 @@ __global__ void __launch_bounds__(NT) k_decode_merge(const DecodeArgs a) {
     float L = 0.f;
     for (int s = 0; s < ns; s++) {
       const float *r = rec + ((size_t)s * g + tid) * rs;
-      if (r[1] > 0.f) L += r[1] * __expf(r[0] - M);
+      if (r[1] > 0.f) L += r[1] * ex2(r[0] - M);
     }
     fac[tid][0] = M;
     fac[tid][1] = L;
@@ -1115,7 +1136,7 @@ __global__ void __launch_bounds__(NT) k_decode_merge(const DecodeArgs a) {
     float v = 0.f;
     for (int s = 0; s < ns; s++) {
       const float *r = rec + ((size_t)s * g + hh) * rs;
-      if (r[1] > 0.f) v += __expf(r[0] - fac[hh][0]) * r[2 + t];
+      if (r[1] > 0.f) v += ex2(r[0] - fac[hh][0]) * r[2 + t];
     }
     if (t < rsV)
       op[hh][t] = v;
