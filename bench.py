@@ -108,7 +108,15 @@ def fold_bytes(U, n, b, kK, kV, kKp, kVp, coord_b, kv_b):
 
 
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers every kernel includes
+    (a change in either changes the compiled kernel)."""
+    h = hashlib.sha256(open(path, "rb").read())
+    csrc = os.path.dirname(path)
+    for inc in ("iskv_internal.hpp", "fold_common.hpp"):
+        q = os.path.join(csrc, inc)
+        if os.path.basename(path).endswith(".hip") and os.path.exists(q):
+            h.update(open(q, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, nunits):

@@ -193,14 +193,14 @@ __device__ __forceinline__ uint32_t int_bf16(int x) { return __float_as_uint((fl
 
 // eight int8 codes (two dwords, low byte first) as eight bf16 values packed in
 // four dwords, the operand layout of the bf16 matrix-core instructions
-// (each byte flipped to q + 128, converted from its byte lane, less 128: exact;
-// the upper halves of two such floats are their bf16 values)
+// (each code sign-extended and converted from its byte lane in one instruction,
+// exact; the upper halves of two such floats are their bf16 values)
 __device__ __forceinline__ void i8x8_bf16(uint32_t w0, uint32_t w1, uint32_t out[4]) {
 #pragma unroll
   for (int e = 0; e < 4; e += 2) {
-    const uint32_t w = (e == 0 ? w0 : w1) ^ 0x80808080u;
-    const float f0 = (float)(w & 0xffu) - 128.f, f1 = (float)((w >> 8) & 0xffu) - 128.f;
-    const float f2 = (float)((w >> 16) & 0xffu) - 128.f, f3 = (float)(w >> 24) - 128.f;
+    const uint32_t w = e == 0 ? w0 : w1;
+    const float f0 = (float)(int8_t)w, f1 = (float)(int8_t)(w >> 8);
+    const float f2 = (float)(int8_t)(w >> 16), f3 = (float)(int8_t)(w >> 24);
     out[e] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     out[e + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
   }
