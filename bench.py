@@ -894,16 +894,9 @@ def full_run_bench(args, w):
     final_bytes = decode_bytes(U, w.group, n, e, kK, kV, coord_b, kv_b, scale_b=scale_b)
 
     rows_folded = 2 * U * n_final
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    if os.path.exists(tpath):
-        try:
-            tr = json.load(open(tpath))
-            src = os.path.join(ROOT, "incremental_rank_svd_amd", "csrc", "k_decode.hip")
-            if tr.get("source_sha256_16") == source_hash(src) and tr.get("workload") == w.name:
-                traffic = tr.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    # HBM bytes per decode launch from a committed counter summary of this
+    # workload's kernels (none is committed for the full run: null)
+    traffic = measured_traffic(w.name).get("k_decode_unit")
 
     res = {
         "metric": METRIC,
