@@ -124,6 +124,8 @@ struct OneshotArgs {
   int batch, kvh, nl_in, lrel0, nl;
   int u0, nrows;
   int ncap;  // history capacity (rows per unit of the int8 scale arrays)
+  int gram;  // 1: R comes from the Cholesky factor of the fp64 Gram matrix (k_oneshot_gram)
+  int cb;    // bytes per coordinate element (the Gram scratch sits in each unit's coordinates)
   uint32_t *status;
 };
 

@@ -933,6 +933,146 @@ __device__ __forceinline__ void tsqr_step(float *A, int ld, float *tau) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cholesky-QR of long prompts. The R factor of a unit's rows X (nrows x 128)
+// is also the Cholesky factor of G = X^T X, and bf16 or fp32 rows are exact in
+// fp64, so G accumulated in fp64 on matrix cores (v_mfma_f64_16x16x4_f64) is
+// correct to fp64 rounding; its Cholesky factor then takes 128 steps instead
+// of one reflector per row of the blockwise QR. In fp64 the Gram matrix costs
+// a singular value sigma_j an absolute error near 1e-16 sigma_1^2 / sigma_j.
+// A pivot at or below 1e-13 of G's largest diagonal entry (a column within
+// about 3e-7 of the largest column norm of the span of the earlier ones, as in
+// rows of lower rank than 128) leaves a zero row of R, which the Jacobi treats
+// as negligible, like the QR's rows beyond the rank; dividing by such a pivot
+// would magnify the rounding of G instead.
+//
+// k_oneshot_gram: one workgroup per unit stream (grid (units, 2)). Rows are
+// staged 64 at a time in LDS as fp32; the 36 upper-triangle 16 x 16 tiles of
+// G are shared out over the 4 waves (9 each, fixed at compile time so the
+// operands stay in registers); lane l feeds row r + l / 16, column
+// 16 t + l % 16 to both operands (A = X^T tile, B = X tile). G (128 x 128,
+// symmetric, fp64) is written to the start of the unit's coordinate region,
+// which the coordinates kernel overwrites afterwards.
+// ---------------------------------------------------------------------------
+constexpr int GCH = 64;      // rows per staged chunk
+constexpr int GXS = D + 4;   // staged row stride (floats)
+
+__device__ __forceinline__ double *gram_scratch(const Stream &X, int u, int cb) {
+  const uintptr_t p = (uintptr_t)((char *)X.C + (size_t)u * X.cstride * cb);
+  return (double *)((p + 7) & ~(uintptr_t)7);
+}
+
+typedef __attribute__((ext_vector_type(4))) double g64x4;
+
+// upper-triangle tile e, row-major over ti <= tj
+struct GTile {
+  int ti, tj;
+};
+constexpr GTile gram_tile(int e) {
+  int tj = 0;
+  while ((tj + 1) * (tj + 2) / 2 <= e) tj++;
+  return GTile{e - tj * (tj + 1) / 2, tj};
+}
+
+template <typename TK, int W>
+__device__ __forceinline__ void oneshot_gram_wave(const OneshotArgs &a, const TK *src, float *xs, double *G) {
+  constexpr int NTILE = 9;  // 36 tiles / 4 waves
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, lk = lane >> 4;
+  g64x4 acc[NTILE];
+#pragma unroll
+  for (int m = 0; m < NTILE; m++) acc[m] = g64x4{0.0, 0.0, 0.0, 0.0};
+  constexpr int PE = 16 / (int)sizeof(TK);  // elements per 16-byte piece
+  for (int r0 = 0; r0 < a.nrows; r0 += GCH) {
+    __syncthreads();
+    for (int idx = tid; idx < GCH * (D / PE); idx += NT) {
+      const int i = idx / (D / PE), c = idx - i * (D / PE);
+      float v[PE];
+#pragma unroll
+      for (int e = 0; e < PE; e++) v[e] = 0.f;
+      if (r0 + i < a.nrows) {
+        const uint4 w = *(const uint4 *)(src + (size_t)(r0 + i) * D + PE * c);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        if constexpr (PE == 8) {
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            v[2 * e] = __uint_as_float(ww[e] << 16);
+            v[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = __uint_as_float(ww[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < PE; e++) xs[i * GXS + PE * c + e] = v[e];
+    }
+    __syncthreads();
+    for (int k0 = 0; k0 < GCH; k0 += 4) {
+      double x[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; t++) x[t] = (double)xs[(k0 + lk) * GXS + 16 * t + l16];
+#pragma unroll
+      for (int m = 0; m < NTILE; m++) {
+        constexpr int dummy = 0;
+        const GTile g = gram_tile(W + 4 * m + dummy);
+        acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[g.ti], x[g.tj], acc[m], 0, 0, 0);
+      }
+    }
+  }
+  // element v of lane l: G[16 ti + l / 16 + 4 v][16 tj + l % 16], mirrored
+#pragma unroll
+  for (int m = 0; m < NTILE; m++) {
+    const GTile g = gram_tile(W + 4 * m);
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int i = 16 * g.ti + lk + 4 * v, j = 16 * g.tj + l16;
+      G[(size_t)i * D + j] = acc[m][v];
+      G[(size_t)j * D + i] = acc[m][v];
+    }
+  }
+}
+
+template <typename TK>
+__global__ void __launch_bounds__(NT) k_oneshot_gram(const OneshotArgs a) {
+  __shared__ float xs[GCH * GXS];
+  const int ul = blockIdx.x, u = a.u0 + ul;
+  const int lrel = ul / (a.batch * a.kvh), rem = ul - lrel * (a.batch * a.kvh);
+  const int bi = rem / a.kvh, hh = rem - bi * a.kvh;
+  const int xk = blockIdx.y, wv = threadIdx.x >> 6;
+  const TK *src = (const TK *)a.src[xk] + (((size_t)bi * a.nl_in + a.lrel0 + lrel) * a.kvh + hh) * (size_t)a.nrows * D;
+  double *G = gram_scratch(a.X[xk], u, a.cb);
+  switch (wv) {
+    case 0: oneshot_gram_wave<TK, 0>(a, src, xs, G); break;
+    case 1: oneshot_gram_wave<TK, 1>(a, src, xs, G); break;
+    case 2: oneshot_gram_wave<TK, 2>(a, src, xs, G); break;
+    default: oneshot_gram_wave<TK, 3>(a, src, xs, G); break;
+  }
+}
+
+// Cholesky G = R^T R in LDS (fp64, R upper triangular in place, row j of R in
+// row j of Gs); a pivot at or below 1e-13 of the largest diagonal entry leaves
+// row j zero
+__device__ __forceinline__ void gram_cholesky(double *Gs) {
+  const int tid = threadIdx.x;
+  double gmax = 0.0;
+  for (int j = 0; j < D; j++) gmax = fmax(gmax, Gs[(size_t)j * D + j]);
+  const double tol = 1e-13 * gmax;
+  for (int j = 0; j < D; j++) {
+    const double d = Gs[(size_t)j * D + j];
+    const double rjj = d > tol ? sqrt(d) : 0.0;
+    const double inv = rjj > 0.0 ? 1.0 / rjj : 0.0;
+    __syncthreads();  // every thread has read the pivot before row j changes
+    if (tid >= j && tid < D) Gs[(size_t)j * D + tid] = (tid == j) ? rjj : Gs[(size_t)j * D + tid] * inv;
+    __syncthreads();
+    const int m = D - 1 - j;
+    for (int idx = tid; idx < m * m; idx += NT) {
+      const int i = j + 1 + idx / m, k = j + 1 + idx % m;
+      if (i <= k) Gs[(size_t)i * D + k] -= Gs[(size_t)j * D + i] * Gs[(size_t)j * D + k];
+    }
+    __syncthreads();
+  }
+}
+
 template <typename TK, int XK>
 __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
   const Stream &X = a.X[XK];
@@ -950,6 +1090,30 @@ __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
   int *perm = (int *)(sgn + D);
   float *Zb = smem;
   const int mz = ldz(OS_M);
+  if (a.gram) {
+    // G into LDS (fp64, 128 x 128 over the QR's region), R by Cholesky, R in
+    // fp32 through global memory behind G, then into R's place in Zb
+    double *G = gram_scratch(X, u, a.cb);
+    float *Rg = (float *)(G + D * D);
+    double *Gs = (double *)smem;
+    for (int idx = tid; idx < D * D; idx += NT) Gs[idx] = G[idx];
+    __syncthreads();
+    gram_cholesky(Gs);
+    for (int idx = tid; idx < D * D; idx += NT) {
+      const int row = idx / D, col = idx - row * D;
+      Rg[idx] = row <= col ? (float)Gs[idx] : 0.f;
+    }
+    __threadfence();
+    __syncthreads();
+    for (int idx = tid; idx < D * D; idx += NT) {
+      const int col = idx / D, row = idx - col * D;
+      Zb[(size_t)col * mz + row] = Rg[(size_t)row * D + col];
+    }
+    __syncthreads();
+    // the scratch lies in the coordinate region, rows past the prompt included:
+    // clear it rather than leave fp64 bit patterns there
+    for (int idx = tid; idx < D * D * 3 / 2; idx += NT) G[idx] = 0.0;
+  } else {
   for (int idx = tid; idx < D * mz; idx += NT) Zb[idx] = 0.f;
   __syncthreads();
   for (int r0 = 0; r0 < a.nrows; r0 += D) {
@@ -960,6 +1124,7 @@ __device__ void oneshot_svd_body(const OneshotArgs &a, float *smem) {
     }
     __syncthreads();
     tsqr_step(Zb, mz, tau);  // R's rows below its diagonal stay zero; the block rows are reloaded
+  }
   }
   // R^T (R's rows as columns) into the Jacobi layout through registers, H = I
   const int c = D, sj = jac_stride(D), rl = jac_rl(D);
@@ -1207,9 +1372,25 @@ hipError_t launch_core(const FoldArgs &a0, int nunits, int kv_bf16, int coord_bf
   return launch_core_nr<float, float>(a, nunits, s);
 }
 
-hipError_t launch_oneshot(const OneshotArgs &a, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
+hipError_t launch_oneshot(const OneshotArgs &a0, int nunits, int kv_bf16, int coord_bf16, hipStream_t s) {
   const size_t lds1 = sizeof(float) * ((size_t)oneshot_small() + 4 * D);
   hipError_t e;
+  // long prompts: R from the Cholesky factor of the fp64 Gram matrix, which
+  // (with R in fp32 behind it) is kept in the units' coordinate regions, when
+  // they can hold it, and read from 16-byte aligned rows
+  OneshotArgs a = a0;
+  a.cb = a.X[0].cs ? 1 : coord_bf16 ? 2 : 4;
+  const size_t need = (size_t)D * D * (sizeof(double) + sizeof(float)) + 8;
+  a.gram = a.nrows >= 1024 && (((uintptr_t)a.src[0] | (uintptr_t)a.src[1]) & 15) == 0 &&
+           a.X[0].cstride * a.cb >= need && a.X[1].cstride * a.cb >= need;
+  if (a.gram) {
+    if (kv_bf16)
+      hipLaunchKernelGGL(k_oneshot_gram<uint16_t>, dim3(nunits, 2), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_oneshot_gram<float>, dim3(nunits, 2), dim3(NT), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (kv_bf16) {
     e = hipFuncSetAttribute((const void *)k_oneshot_svd<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
     if (e != hipSuccess) return e;
