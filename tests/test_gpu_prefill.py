@@ -125,27 +125,36 @@ def test_prefill_oneshot_argument_and_state_checks(iskv):
     assert cache.status() == 0
 
 
-def test_prefill_oneshot_rank_deficient_rows(iskv):
+@pytest.mark.parametrize("nrows,max_tokens", [
+    (200, 300),    # blockwise QR
+    (2048, 8192),  # Cholesky-QR of the Gram matrix (pivots of rounding give zero rows)
+])
+def test_prefill_oneshot_rank_deficient_rows(iskv, nrows, max_tokens):
     """Rows of rank 3 under a rank budget of 8: the five extra basis vectors
     are completed orthonormally; the history equals the rows."""
     # fp32 rows: in bf16 the rounding itself would lift the rank to d
     w = replace(synth.get_config(3), layers=1, kv_heads=1, q_heads=4, rank_k=8, rank_v=8, prefill_blocks=0,
-                decode_tokens=300, kv_dtype="f32", coord_dtype="f32", cfg_id=58)
-    rows = _rows(w, 300)
+                decode_tokens=max_tokens, kv_dtype="f32", coord_dtype="f32", cfg_id=58)
+    note("case: rank-3 one-shot prefill nrows=%d" % nrows)
+    rows = _rows(w, nrows)
     rng = np.random.default_rng(5)
-    rows["K"][0, 0, 0] = rng.standard_normal((300, 3)) @ rng.standard_normal((3, D))
-    cache = iskv.Cache(iskv.config_from_workload(w), device=DEV)
+    rows["K"][0, 0, 0] = rng.standard_normal((nrows, 3)) @ rng.standard_normal((3, D))
+    cache = iskv.Cache(iskv.config_from_workload(w, max_tokens=max_tokens), device=DEV)
     K = to_dev(rows["K"], torch.float32, DEV)
     V = to_dev(rows["V"], torch.float32, DEV)
-    cache.prefill_oneshot(K[:, :, :, :200].contiguous(), V[:, :, :, :200].contiguous())
+    cache.prefill_oneshot(K.contiguous(), V.contiguous())
     assert cache.status() == 0
     C, sig, Bt, W, n, e, k = unit_state(cache, 0, 0, 0, 0)
-    assert (n, e, k) == (200, 0, 8)
+    assert (n, e, k) == (nrows, 0, 8)
     assert np.abs(Bt[:k] @ Bt[:k].T - np.eye(k)).max() < 1e-5
     X = cache.reconstruct(0, 0, 0, 0).cpu().double().numpy()
-    ref = K[0, 0, 0, :200].double().cpu().numpy()
+    ref = K[0, 0, 0].double().cpu().numpy()
     assert np.linalg.norm(X - ref) <= 1e-5 * np.linalg.norm(ref)
     assert sig[3:k].max() <= 1e-5 * sig[0]
+    # the values (full rank) against the oracle
+    st = oracle.UnitState.empty(D, w.block, 8, max_tokens)
+    st.prefill_oneshot(rows["V"][0, 0, 0])
+    check_unit(cache, 1, 0, 0, 0, st, label=("rank-deficient keys, values", nrows))
 
 
 def test_prefill_oneshot_layer_subset(iskv):
