@@ -554,14 +554,15 @@ def prefill_bench(args):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     res = {}
-    for mode in ("oneshot", "blocks"):
+    # the first one-shot call (on its own cache) loads the kernels; the second is timed
+    for mode in ("warmup", "oneshot", "blocks"):
         cache = iskv.Cache(iskv.config_from_workload(w), device=dev)
         h = cache.h
         blocks = [(K[:, :, :, s:s + w.block].contiguous(), V[:, :, :, s:s + w.block].contiguous())
                   for s in range(0, P, w.block)] if mode == "blocks" else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        if mode == "oneshot":
+        if mode in ("warmup", "oneshot"):
             rc = lib.iskv_prefill_oneshot(h, ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()), P, 0,
                                           w.layers, sp)
             if rc:

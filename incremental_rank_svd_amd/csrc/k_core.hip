@@ -982,39 +982,48 @@ __device__ __forceinline__ void oneshot_gram_wave(const OneshotArgs &a, const TK
 #pragma unroll
   for (int m = 0; m < NTILE; m++) acc[m] = g64x4{0.0, 0.0, 0.0, 0.0};
   constexpr int PE = 16 / (int)sizeof(TK);  // elements per 16-byte piece
+  constexpr int NP = GCH * (D / PE) / NT;   // pieces per thread and chunk
+  static_assert(NP * NT == GCH * (D / PE), "whole pieces per thread");
+  // the next chunk's pieces are loaded into registers while the matrix cores
+  // work on the current one
+  uint4 nx[NP];
+  auto fetch = [&](int r0) {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      const int idx = tid + NT * p, i = idx / (D / PE), c = idx - i * (D / PE);
+      nx[p] = (r0 + i < a.nrows) ? *(const uint4 *)(src + (size_t)(r0 + i) * D + PE * c) : uint4{0, 0, 0, 0};
+    }
+  };
+  fetch(0);
   for (int r0 = 0; r0 < a.nrows; r0 += GCH) {
-    __syncthreads();
-    for (int idx = tid; idx < GCH * (D / PE); idx += NT) {
-      const int i = idx / (D / PE), c = idx - i * (D / PE);
+    __syncthreads();  // the previous chunk is no longer read
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      const int idx = tid + NT * p, i = idx / (D / PE), c = idx - i * (D / PE);
+      const uint32_t ww[4] = {nx[p].x, nx[p].y, nx[p].z, nx[p].w};
       float v[PE];
+      if constexpr (PE == 8) {
 #pragma unroll
-      for (int e = 0; e < PE; e++) v[e] = 0.f;
-      if (r0 + i < a.nrows) {
-        const uint4 w = *(const uint4 *)(src + (size_t)(r0 + i) * D + PE * c);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        if constexpr (PE == 8) {
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            v[2 * e] = __uint_as_float(ww[e] << 16);
-            v[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; e++) v[e] = __uint_as_float(ww[e]);
+        for (int e = 0; e < 4; e++) {
+          v[2 * e] = __uint_as_float(ww[e] << 16);
+          v[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] = __uint_as_float(ww[e]);
       }
 #pragma unroll
       for (int e = 0; e < PE; e++) xs[i * GXS + PE * c + e] = v[e];
     }
     __syncthreads();
+    if (r0 + GCH < a.nrows) fetch(r0 + GCH);
     for (int k0 = 0; k0 < GCH; k0 += 4) {
       double x[D / 16];
 #pragma unroll
       for (int t = 0; t < D / 16; t++) x[t] = (double)xs[(k0 + lk) * GXS + 16 * t + l16];
 #pragma unroll
       for (int m = 0; m < NTILE; m++) {
-        constexpr int dummy = 0;
-        const GTile g = gram_tile(W + 4 * m + dummy);
+        const GTile g = gram_tile(W + 4 * m);
         acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[g.ti], x[g.tj], acc[m], 0, 0, 0);
       }
     }
