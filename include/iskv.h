@@ -150,7 +150,10 @@ ISKV_API int iskv_append_block(iskv_t h, const void *k_rows, const void *v_rows,
  * read only. Requires every such layer to be empty (n == 0 and e == 0, else
  * ISKV_ERR_STATE) and nrows <= ncap = floor(max_tokens / b) * b, the history
  * capacity in whole blocks (else ISKV_ERR_CAPACITY). nrows need not be a
- * multiple of b. Later appends fold into this history as usual. */
+ * multiple of b. Later appends fold into this history as usual. Long
+ * prompts (nrows >= 1024, 16-byte aligned rows) are factorised through the
+ * fp64 Gram matrix, kept in these layers' own (empty) coordinate storage when
+ * it holds 192 KiB per stream; no memory is allocated. */
 ISKV_API int iskv_prefill_oneshot(iskv_t h, const void *k_rows, const void *v_rows, int32_t nrows,
                                   int32_t layer0, int32_t nlayers, void *stream);
 
