@@ -39,11 +39,12 @@ def _rows(w, ntok):
 
 
 @pytest.mark.parametrize("nrows,rk,rv,coord", [
-    (1000, 32, 48, "f32"),   # several 128-row QR blocks and a ragged tail
+    (1000, 32, 48, "f32"),   # several 128-row QR blocks and a ragged tail (blockwise QR)
     (40, 64, 64, "f32"),     # fewer rows than d: k = nrows, exact
     (128, 128, 128, "f32"),  # untruncated, one full block
     (700, 32, 32, "bf16"),   # bf16 coordinates
-    (8192, 32, 48, "f32"),   # 64 QR blocks
+    (8192, 32, 48, "f32"),   # Cholesky-QR of the Gram matrix
+    (4096, 32, 48, "bf16"),  # Cholesky-QR, bf16 coordinates
 ])
 def test_prefill_oneshot_matches_oracle(iskv, nrows, rk, rv, coord):
     extra = 300
